@@ -1,0 +1,236 @@
+"""CPU fp64 oracle: exact attention over a paged KV cache, written as its plain definition.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check of the entry module and the
+CPU-baseline leg of the bench use it.  It shares no code with the HIP library.
+
+What it computes (for sequence b, head h, query row i of that sequence):
+
+    K_b[t] = k_pool[ block_table[b, t // page_size], t % page_size ]
+    V_b[t] = v_pool[ block_table[b, t // page_size], t % page_size ]
+    s_it   = scale * < Q[b, i, h, :], K_b[t, h, :] >
+    O[b, i, h, :] = sum_{t visible} softmax_t(s_it) * V_b[t, h, :]
+
+Sources, by page title and section:
+  * "FlashAttention and PagedAttention: Two Fixes for Two Different
+    Bottlenecks", section "Why attention is costly": the attention formula
+    softmax(Q K^T / sqrt(d)) V.
+  * "Flash Attention: Fast, Memory-Efficient Attention for LLMs", section
+    "Standard Attention: The Memory Problem" (flowchart S = Q K^T,
+    P = softmax(S), O = P V): the three-step unfused definition, which this
+    oracle follows literally, materialising complete rows of S and P.
+  * "What is Paged FlashAttention?", sections "How does it work?" and
+    "Practical example": the block-table translation logical = pos // page_size,
+    offset = pos % page_size, physical = block_table[logical].
+  * Same page, "Does it change the attention result or complexity?", and the
+    first page's "How it works": the tiled method reaches exactly this result up
+    to rounding, so this plain definition is the reference.
+
+Readings where the pages leave a step open:
+  * Causal alignment for a chunk of q_len rows over L keys is bottom-right:
+    query row i sits at absolute position L - q_len + i and sees keys t <= that
+    position (the pages only name a causal flag that skips future tokens).
+  * A decode query is the newest token, already appended to the cache, and
+    sees all L keys of its sequence (KV-cache flowchart, "Append new K_t, V_t").
+  * The scale is the fp32 value handed to the kernel, widened exactly to fp64.
+
+Inputs are raw bf16 bit patterns (uint16 arrays).  Decoding them to fp64 is
+exact.  The output stays in fp64; nothing here rounds to bf16.
+
+Parity status: pinned (see tests/test_oracle_pins.py for each pin).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+# rows of S materialised at once; every row is always complete over its keys
+ROW_BLOCK = 1024
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (upper half of a binary32) to fp64."""
+    bits = np.asarray(bits)
+    if bits.dtype != np.uint16:
+        raise TypeError("bf16 inputs are passed as uint16 bit patterns")
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pages_needed(seq_len: int, page_size: int) -> int:
+    """Number of pages a sequence of seq_len tokens occupies: ceil(L / page_size).
+
+    "Flash Attention: Fast, Memory-Efficient Attention for LLMs", section
+    "PagedAttention (vLLM)", flowchart: a 200-token request in 16-token pages
+    fills 13 pages, the last one partly.
+    """
+    return -(-int(seq_len) // int(page_size))
+
+
+def locate_token(block_table_row: Sequence[int], t: int, page_size: int):
+    """Block-table translation of token position t.
+
+    "What is Paged FlashAttention?", section "Practical example": logical page
+    is the quotient of the position by the page size, the offset is the
+    remainder, and the physical page is the table entry at the logical page.
+    Returns (logical, offset, physical).
+    """
+    logical = t // page_size
+    offset = t % page_size
+    physical = int(block_table_row[logical])
+    return logical, offset, physical
+
+
+def gather_sequence(pool_bits: np.ndarray, block_table_row: Sequence[int],
+                    seq_len: int, page_size: int) -> np.ndarray:
+    """Reads the seq_len tokens of one sequence out of the paged pool, token by token.
+
+    pool_bits: uint16 [num_pages, page_size, heads, d].  Returns fp64 [L, heads, d].
+    Only the slots the block table names for tokens 0..L-1 are read; tail slots
+    and unused pages are never touched.
+    """
+    num_pages = pool_bits.shape[0]
+    if pool_bits.shape[1] != page_size:
+        raise ValueError("pool page dimension does not match page_size")
+    rows = np.empty((seq_len,) + tuple(pool_bits.shape[2:]), dtype=np.uint16)
+    for t in range(seq_len):
+        _, offset, physical = locate_token(block_table_row, t, page_size)
+        if not 0 <= physical < num_pages:
+            raise IndexError(f"token {t}: physical page {physical} outside pool of {num_pages}")
+        rows[t] = pool_bits[physical, offset]
+    return bf16_to_f64(rows)
+
+
+def visible_mask(positions: np.ndarray, seq_len: int, causal: bool) -> np.ndarray:
+    """Boolean [rows, L]: key t is visible to a query at absolute position p.
+
+    Non-causal: every key 0 <= t < L.  Causal: keys t <= p (bottom-right
+    alignment; see the module docstring).
+    """
+    keys = np.arange(seq_len)
+    if not causal:
+        return np.ones((len(positions), seq_len), dtype=bool)
+    return keys[None, :] <= np.asarray(positions)[:, None]
+
+
+def scores(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * Q K^T for one head: q_rows [r, d], keys [L, d] -> [r, L]."""
+    return scale * (q_rows @ keys.T)
+
+
+def softmax_rows(s: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Row softmax over the visible keys, two passes (max, then exp and sum).
+
+    Masked entries get probability exactly 0.  Each row must have at least one
+    visible key.
+    """
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("a query row has no visible key")
+    e = np.exp(s - m)
+    total = e.sum(axis=1, keepdims=True)
+    p = e / total
+    if np.max(np.abs(p.sum(axis=1) - 1.0)) > 1e-12:
+        raise AssertionError("softmax rows do not sum to 1")
+    return p, m[:, 0] + np.log(total[:, 0])
+
+
+def weighted_values(p: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """O = P V for one head: p [r, L], values [L, d] -> [r, d]."""
+    return p @ values
+
+
+def attend(q_rows: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
+           positions: np.ndarray, causal: bool, scale: float):
+    """Attention of some query rows of one sequence over its gathered keys.
+
+    q_rows [r, H, d] fp64, k_seq / v_seq [L, H, d] fp64, positions [r] absolute.
+    Returns (O [r, H, d] fp64, lse [r, H] fp64 natural-log sum of exp).
+    """
+    r, heads, d = q_rows.shape
+    seq_len = k_seq.shape[0]
+    out = np.empty((r, heads, d), dtype=np.float64)
+    lse = np.empty((r, heads), dtype=np.float64)
+    for h in range(heads):
+        for r0 in range(0, r, ROW_BLOCK):
+            r1 = min(r, r0 + ROW_BLOCK)
+            mask = visible_mask(positions[r0:r1], seq_len, causal)
+            s = scores(q_rows[r0:r1, h, :], k_seq[:, h, :], scale)
+            p, row_lse = softmax_rows(s, mask)
+            out[r0:r1, h, :] = weighted_values(p, v_seq[:, h, :])
+            lse[r0:r1, h] = row_lse
+    return out, lse
+
+
+def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_start,
+                  causal: bool, scale: float, rows: Optional[dict] = None):
+    """Prefill (or chunked prefill) over a paged cache.
+
+    q_bits       uint16 [total_q, H, d]; rows of sequence b are q_start[b]..q_start[b+1]-1
+    k/v_pool_bits uint16 [num_pages, page_size, H, d]
+    block_table  int [batch, max_pages_per_seq]
+    seq_lens     int [batch]: L_b, the KV length including this chunk
+    scale        the fp32 scale value (widened exactly)
+    rows         optional {b: array of local row indices} to evaluate only some rows
+
+    Returns (O fp64 [total_q, H, d] with NaN where not evaluated, lse [total_q, H]).
+    """
+    q_bits = np.asarray(q_bits)
+    total_q, heads, d = q_bits.shape
+    page_size = k_pool_bits.shape[1]
+    scale = float(np.float32(scale))
+    out = np.full((total_q, heads, d), np.nan)
+    lse = np.full((total_q, heads), np.nan)
+    for b in range(len(seq_lens)):
+        seq_len = int(seq_lens[b])
+        start, stop = int(q_start[b]), int(q_start[b + 1])
+        q_len = stop - start
+        if q_len == 0:
+            continue
+        if not 1 <= q_len <= seq_len:
+            raise ValueError(f"sequence {b}: need 1 <= q_len ({q_len}) <= L ({seq_len})")
+        if rows is not None and b not in rows:
+            continue
+        local = np.arange(q_len) if rows is None else np.asarray(rows[b], dtype=np.int64)
+        k_seq = gather_sequence(k_pool_bits, block_table[b], seq_len, page_size)
+        v_seq = gather_sequence(v_pool_bits, block_table[b], seq_len, page_size)
+        positions = seq_len - q_len + local
+        q_rows = bf16_to_f64(q_bits[start + local])
+        o, l = attend(q_rows, k_seq, v_seq, positions, causal, scale)
+        out[start + local] = o
+        lse[start + local] = l
+    return out, lse
+
+
+def paged_decode(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, scale: float,
+                 seqs: Optional[Sequence[int]] = None):
+    """Decode: one query token per sequence over all L_b cached keys (itself included).
+
+    q_bits uint16 [batch, H, d].  Returns (O fp64 [batch, H, d], lse [batch, H]);
+    sequences not in `seqs` are left NaN.
+    """
+    q_bits = np.asarray(q_bits)
+    batch, heads, d = q_bits.shape
+    page_size = k_pool_bits.shape[1]
+    scale = float(np.float32(scale))
+    out = np.full((batch, heads, d), np.nan)
+    lse = np.full((batch, heads), np.nan)
+    for b in (range(batch) if seqs is None else seqs):
+        seq_len = int(seq_lens[b])
+        if seq_len < 1:
+            raise ValueError(f"sequence {b}: decode needs L >= 1")
+        k_seq = gather_sequence(k_pool_bits, block_table[b], seq_len, page_size)
+        v_seq = gather_sequence(v_pool_bits, block_table[b], seq_len, page_size)
+        q_rows = bf16_to_f64(q_bits[b:b + 1])
+        o, l = attend(q_rows, k_seq, v_seq, np.array([seq_len - 1]), False, scale)
+        out[b] = o[0]
+        lse[b] = l[0]
+    return out, lse
+
+
+__all__ = [
+    "bf16_to_f64", "pages_needed", "locate_token", "gather_sequence", "visible_mask",
+    "scores", "softmax_rows", "weighted_values", "attend", "paged_prefill", "paged_decode",
+    "ROW_BLOCK",
+]

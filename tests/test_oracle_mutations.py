@@ -1,0 +1,97 @@
+"""Plants plausible mistakes in the oracle (on the CPU, one at a time) and checks
+that at least one pin catches each: evidence that the pins constrain every step
+of the oracle, not just that it agrees with itself."""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from tests import oracle_pins as P
+
+
+def _swap_quotient_remainder(row, t, ps):
+    return t % ps, t // ps, int(row[t % ps]) if t % ps < len(row) else -1
+
+
+def _ignore_table(row, t, ps):
+    return t // ps, t % ps, t // ps
+
+
+def _offset_off_by_one(row, t, ps):
+    return t // ps, (t + 1) % ps, int(row[t // ps])
+
+
+def _causal_strict(positions, L, causal):
+    keys = np.arange(L)
+    if not causal:
+        return np.ones((len(positions), L), dtype=bool)
+    return keys[None, :] < np.asarray(positions)[:, None]
+
+
+def _causal_top_left(positions, L, causal):
+    keys = np.arange(L)
+    if not causal:
+        return np.ones((len(positions), L), dtype=bool)
+    pos = np.asarray(positions)
+    # forgets the L - q_len shift: row index instead of absolute position
+    return keys[None, :] <= (pos - pos.min())[:, None]
+
+
+def _no_scale(q, keys, scale):
+    return q @ keys.T
+
+
+def _scale_squared(q, keys, scale):
+    return scale * scale * (q @ keys.T)
+
+
+def _mask_after_softmax(s, mask):
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    p = np.where(mask, p, 0.0)
+    return p, m[:, 0]
+
+
+def _softmax_sign_flip(s, mask):
+    return A.softmax_rows.__wrapped__(-s, mask) if hasattr(A.softmax_rows, "__wrapped__") else \
+        _ORIG["softmax_rows"](-s, mask)
+
+
+def _values_from_keys_layout(p, values):
+    # transposed operand: contracts over the wrong axis of a square-ish block
+    return p @ values[::-1]
+
+
+def _wrong_bf16_shift(bits):
+    bits = np.asarray(bits)
+    return (bits.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+
+
+_ORIG = {name: getattr(A, name) for name in
+         ("locate_token", "visible_mask", "scores", "softmax_rows", "weighted_values", "bf16_to_f64")}
+
+MUTANTS = [
+    ("locate_token", _swap_quotient_remainder),
+    ("locate_token", _ignore_table),
+    ("locate_token", _offset_off_by_one),
+    ("visible_mask", _causal_strict),
+    ("visible_mask", _causal_top_left),
+    ("scores", _no_scale),
+    ("scores", _scale_squared),
+    ("softmax_rows", _mask_after_softmax),
+    ("softmax_rows", _softmax_sign_flip),
+    ("weighted_values", _values_from_keys_layout),
+    ("bf16_to_f64", _wrong_bf16_shift),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTANTS, ids=[f"{n}:{f.__name__}" for n, f in MUTANTS])
+def test_some_pin_catches_mutant(monkeypatch, name, fn):
+    monkeypatch.setattr(A, name, fn)
+    results = P.run_all_pins()
+    assert not all(results.values()), f"no pin caught mutant {fn.__name__}: {results}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    results = P.run_all_pins()
+    assert all(results.values()), results

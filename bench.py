@@ -1,0 +1,362 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Default workload: decode_64 (64 sequences x 1 query token, 32 heads, d=128,
+lengths uniform on {512..8192}, 16-token pages in a shuffled pool).  One step is
+one pa_decode over the batch (the split pass and the combine pass, issued as
+pa_decode_partial + pa_decode_combine so each kernel can be timed with HIP events
+on the stream it runs on).  `value` is algorithmic KV bytes per second over whole
+steps; `roofline` rates the split kernel alone against 8 TB/s.  A `prefill` object
+times the causal N=4096 prefill (32 heads, d=128) against the 2.5 PFLOP/s dense
+bf16 MFMA peak.  `cpu_baseline` times the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn prefill TFLOP/s and decode KV GB/s on 1 MI355X (% of roofline)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_pa_amd", "csrc")
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "device_util.h", "kernels.h"],
+    "prefill": ["prefill.hip", "device_util.h", "kernels.h"],
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic work
+
+def visible_pairs(seq_lens, q_lens, causal: bool) -> int:
+    """Visible (query, key) pairs per head; causal is bottom-right aligned."""
+    total = 0
+    for L, n in zip(seq_lens, q_lens):
+        L, n = int(L), int(n)
+        if causal:
+            total += n * (L - n + 1) + n * (n - 1) // 2
+        else:
+            total += n * L
+    return total
+
+
+def prefill_work(wl, call):
+    """(FLOPs, bytes): 4*d*Hq per visible pair; Q + O + valid K/V read or written once."""
+    q_lens = call.q_start_host[1:] - call.q_start_host[:-1]
+    hq = call.q.shape[1]
+    d = wl.head_dim
+    flops = 4 * d * hq * visible_pairs(call.seq_lens_host, q_lens, call.causal)
+    nbytes = 2 * (2 * int(q_lens.sum()) * hq * d + 2 * int(call.seq_lens_host.sum()) * wl.heads * d)
+    return flops, nbytes
+
+
+def decode_kv_bytes(wl, call) -> int:
+    """K and V bytes of every valid cached token (the decode metric)."""
+    return int(call.seq_lens_host.astype("int64").sum()) * 2 * wl.heads * wl.head_dim * 2
+
+
+# ------------------------------------------------------------------ traffic record
+
+def source_digest(kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if absent or
+    if the kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kind}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_digest(kind):
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ GPU legs
+
+def timed_decode(wl, call, steps, warmup):
+    import torch
+    from exact_tiled_attention_pa_amd import binding as B
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    out = torch.empty_like(call.q)
+    lay = B.layout_of(wl.k_pool, call.block_table)
+
+    def step():
+        B.pa_decode_partial(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
+                            wl.scale, ws)
+        B.pa_decode_combine(call.seq_lens, out, ws, lay)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        B.pa_decode_partial(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
+                            wl.scale, ws)
+        ev[i][1].record()
+        B.pa_decode_combine(call.seq_lens, out, ws, lay)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    return wall, split_ms, comb_ms
+
+
+def timed_prefill(wl, call, steps, warmup):
+    import torch
+    from exact_tiled_attention_pa_amd import binding as B
+    out = torch.empty_like(call.q)
+
+    def run():
+        B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
+                     call.causal, wl.scale, out, call.q_start, call.max_q_len)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [e[0].elapsed_time(e[1]) for e in ev]
+
+
+def prefill_summary(wl, call, steps, warmup):
+    flops, nbytes = prefill_work(wl, call)
+    wall, ms = timed_prefill(wl, call, steps, warmup)
+    avg = sum(ms) / len(ms)
+    tflops = flops / (avg * 1e-3) / 1e12
+    traffic = recorded_traffic("prefill", wl.name)
+    return {
+        "workload": wl.name,
+        "tflops": round(tflops, 2),
+        "kernel_ms_avg": round(avg, 4),
+        "kernel_ms_min": round(min(ms), 4),
+        "ms_per_call_wall": round(wall / steps * 1e3, 4),
+        "flops_per_launch": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "alg_bytes_per_launch": nbytes,
+    }
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline_decode(wl, call, budget_s=15.0):
+    """The oracle as it stands, single BLAS thread, on whole sequences of the same
+    batch until about budget_s seconds of CPU work; reported in GB/s of KV read."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from exact_tiled_attention_pa_amd import workloads as W
+    from oracle import attention as OA
+
+    q = W.to_host_bits(call.q)
+    done_bytes = 0
+    spent = 0.0
+    seqs = []
+    order = list(range(call.batch))
+    with threadpool_limits(limits=1):
+        for b in order:
+            L = int(call.seq_lens_host[b])
+            n = -(-L // wl.page_size)
+            pages = call.block_table_host[b, :n]
+            import torch
+            sel = torch.as_tensor(pages.astype("int64"), device=wl.k_pool.device)
+            k = W.to_host_bits(wl.k_pool.index_select(0, sel))
+            v = W.to_host_bits(wl.v_pool.index_select(0, sel))
+            table = np.full((1, n), -1, dtype=np.int64)
+            table[0] = np.arange(n)
+            t0 = time.perf_counter()
+            OA.paged_decode(q[b:b + 1], k, v, table, call.seq_lens_host[b:b + 1], wl.scale)
+            spent += time.perf_counter() - t0
+            done_bytes += L * 2 * wl.heads * wl.head_dim * 2
+            seqs.append(b)
+            if spent >= budget_s:
+                break
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"oracle (NumPy fp64, 1 BLAS thread) on {len(seqs)} of {call.batch} "
+                  f"decode sequences ({sum(int(call.seq_lens_host[b]) for b in seqs)} "
+                  f"tokens, all {wl.heads} heads) in {spent:.1f} s",
+    }
+
+
+def cpu_baseline_prefill(wl, call, budget_s=15.0):
+    """Oracle on query rows of the first sequence, spread over the whole range."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from exact_tiled_attention_pa_amd import workloads as W
+    from oracle import attention as OA
+
+    q = W.to_host_bits(call.q)
+    k = W.to_host_bits(wl.k_pool)
+    v = W.to_host_bits(wl.v_pool)
+    q_len = int(call.q_start_host[1] - call.q_start_host[0])
+    L = int(call.seq_lens_host[0])
+    n_rows, spent, pairs = 16, 0.0, 0
+    with threadpool_limits(limits=1):
+        while spent < budget_s and n_rows <= q_len:
+            rows = np.linspace(0, q_len - 1, n_rows).astype(np.int64)
+            t0 = time.perf_counter()
+            OA.paged_prefill(q, k, v, call.block_table_host, call.seq_lens_host,
+                             call.q_start_host, call.causal, wl.scale, rows={0: rows})
+            spent = time.perf_counter() - t0
+            pos = L - q_len + rows
+            pairs = int((pos + 1).sum()) if call.causal else L * len(rows)
+            n_rows *= 2
+    hq = call.q.shape[1]
+    flops = 4 * wl.head_dim * hq * pairs
+    return {
+        "value": round(flops / spent / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"oracle (NumPy fp64, 1 BLAS thread) on {n_rows // 2} query rows of "
+                  f"{q_len}, all {hq} heads, in {spent:.1f} s",
+    }
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_64")
+    ap.add_argument("--prefill-workload", default="prefill_4096_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_tiled_attention_pa_amd import binding as B
+    from exact_tiled_attention_pa_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.load_library()
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if args.workload not in W.FULL_WORKLOADS:
+        raise SystemExit(f"unknown workload {args.workload}")
+    log(f"generating {args.workload}")
+    wl = W.FULL_WORKLOADS[args.workload](device="cuda")
+    torch.cuda.synchronize()
+
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16", "data": "synthetic"}
+    call = wl.calls[0]
+    if call.kind == "decode":
+        nbytes = decode_kv_bytes(wl, call)
+        log(f"decode: {call.batch} seqs, {int(call.seq_lens_host.sum())} tokens, "
+            f"{nbytes / 1e9:.3f} GB of K/V per step")
+        wall, split_ms, comb_ms = timed_decode(wl, call, args.steps, args.warmup)
+        ms_step = wall / args.steps * 1e3
+        split_avg = sum(split_ms) / len(split_ms)
+        achieved = nbytes / (split_avg * 1e-3) / 1e9
+        traffic = recorded_traffic("decode", wl.name)
+        result.update({
+            "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(ms_step, 4),
+            "config": {"workload": wl.name, "batch": call.batch, "heads": wl.heads,
+                       "head_dim": wl.head_dim, "page_size": wl.page_size,
+                       "total_tokens": int(call.seq_lens_host.sum()),
+                       "kv_bytes_per_step": nbytes, "description": wl.description},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "kernel": "decode_partial_kernel<128>",
+                         "kernel_ms_avg": round(split_avg, 4),
+                         "combine_ms_avg": round(sum(comb_ms) / len(comb_ms), 4)},
+        })
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle) on a bounded sample")
+            result["cpu_baseline"] = cpu_baseline_decode(wl, call)
+    else:
+        s = prefill_summary(wl, call, args.steps, args.warmup)
+        result.update({
+            "value": s["tflops"], "unit": "TFLOP/s", "ms_per_step": s["ms_per_call_wall"],
+            "config": {"workload": wl.name, "heads": wl.heads, "head_dim": wl.head_dim,
+                       "page_size": wl.page_size, "causal": call.causal,
+                       "description": wl.description},
+            "roofline": dict(s["roofline"], kernel="prefill_kernel",
+                             kernel_ms_avg=s["kernel_ms_avg"]),
+        })
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle) on a bounded sample")
+            result["cpu_baseline"] = cpu_baseline_prefill(wl, call)
+    del wl
+
+    if not args.no_prefill and call.kind == "decode":
+        log(f"prefill leg: {args.prefill_workload}")
+        pw = W.FULL_WORKLOADS[args.prefill_workload](device="cuda")
+        result["prefill"] = prefill_summary(pw, pw.calls[0], args.steps, args.warmup)
+        del pw
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

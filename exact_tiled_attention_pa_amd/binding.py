@@ -1,0 +1,228 @@
+"""Thin ctypes binding of libpagedattn (argument marshalling only).
+
+Every function of the C ABI (include/pagedattn.h) is exposed under the same
+name.  The tensor-level functions check shapes, dtypes and devices on the host,
+pass raw device pointers and torch's current HIP stream, and raise
+PagedAttnError on a non-zero status.  All attention arithmetic happens in the
+HIP kernels of the library; nothing here computes a result, and there is no
+fallback: if the library is missing or no GPU is present, calls fail loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_NULL = 1
+PA_ERR_INVALID_ARG = 2
+PA_ERR_UNSUPPORTED = 3
+PA_ERR_WORKSPACE = 4
+PA_ERR_HIP = 5
+
+# Every symbol the header declares.
+EXPORTED = (
+    "pa_prefill", "pa_decode_workspace_bytes", "pa_decode_split_tokens", "pa_decode",
+    "pa_decode_partial", "pa_decode_combine", "pa_status_string", "pa_last_error",
+    "pa_version",
+)
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)} -- {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class KVLayout(ctypes.Structure):
+    _fields_ = [
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads libpagedattn.so (built in-tree by __graft_entry__.build or
+    `python -m exact_tiled_attention_pa_amd.build`).  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libpagedattn.so not found at {p}; build it first "
+                           "(python -m exact_tiled_attention_pa_amd.build)")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lay = ctypes.POINTER(KVLayout)
+    lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, f32, vp, vp, i32, i32, i32,
+                               lay, vp]
+    lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_decode_workspace_bytes.argtypes = [i32, i32, lay]
+    lib.pa_decode_workspace_bytes.restype = sz
+    lib.pa_decode_split_tokens.argtypes = [lay]
+    lib.pa_decode_split_tokens.restype = i32
+    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, i32, vp, sz, lay, vp]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_partial.argtypes = [vp, vp, vp, vp, vp, f32, i32, i32, vp, sz, lay, vp]
+    lib.pa_decode_partial.restype = ctypes.c_int
+    lib.pa_decode_combine.argtypes = [vp, vp, i32, i32, vp, sz, lay, vp]
+    lib.pa_decode_combine.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return load_library().pa_last_error().decode()
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PagedAttnError(status, last_error())
+
+
+def make_layout(num_pages, page_size, num_kv_heads, head_dim, max_pages_per_seq) -> KVLayout:
+    return KVLayout(int(num_pages), int(page_size), int(num_kv_heads), int(head_dim),
+                    int(max_pages_per_seq))
+
+
+def layout_of(k_pool: torch.Tensor, block_table: torch.Tensor) -> KVLayout:
+    num_pages, page_size, num_kv_heads, head_dim = k_pool.shape
+    return make_layout(num_pages, page_size, num_kv_heads, head_dim, block_table.shape[1])
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_device_tensors(**tensors):
+    dev = None
+    for name, t in tensors.items():
+        _require(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+        _require(t.is_cuda, f"{name} must be on a GPU (got {t.device})")
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+        dev = dev or t.device
+        _require(t.device == dev, f"{name} is on {t.device}, expected {dev}")
+
+
+def pa_prefill(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_start,
+               max_q_len: int, stream=None):
+    """Paged (chunked) prefill: out[q_start[b]:q_start[b+1]] = attention of sequence b's
+    query rows over its L_b = seq_lens[b] paged keys.  See pa_prefill in pagedattn.h."""
+    _check_device_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
+                          seq_lens=seq_lens, out=out, q_start=q_start)
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
+        _require(t.dtype == torch.bfloat16, f"{name} must be bfloat16")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens), ("q_start", q_start)):
+        _require(t.dtype == torch.int32, f"{name} must be int32")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape, "k_pool/v_pool: [P, ps, Hkv, d]")
+    _require(q.dim() == 3 and q.shape[2] == k_pool.shape[3], "q: [total_q, Hq, d]")
+    _require(out.shape == q.shape, "out must have q's shape")
+    batch = seq_lens.numel()
+    _require(block_table.dim() == 2 and block_table.shape[0] >= batch, "block_table: [batch, maxp]")
+    _require(q_start.numel() == batch + 1, "q_start: [batch + 1]")
+    lay = layout_of(k_pool, block_table)
+    st = load_library().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                   _ptr(seq_lens), int(bool(causal)), float(scale), _ptr(out),
+                                   _ptr(q_start), batch, q.shape[1], int(max_q_len),
+                                   ctypes.byref(lay), _stream(stream))
+    _check(st)
+    return out
+
+
+def pa_decode_workspace_bytes(batch: int, num_q_heads: int, layout: KVLayout) -> int:
+    return int(load_library().pa_decode_workspace_bytes(int(batch), int(num_q_heads),
+                                                        ctypes.byref(layout)))
+
+
+def pa_decode_split_tokens(layout: KVLayout) -> int:
+    return int(load_library().pa_decode_split_tokens(ctypes.byref(layout)))
+
+
+def decode_workspace(q, k_pool, block_table) -> torch.Tensor:
+    """Allocates (through torch) a workspace large enough for pa_decode."""
+    n = pa_decode_workspace_bytes(q.shape[0], q.shape[1], layout_of(k_pool, block_table))
+    _require(n > 0, "invalid decode shapes")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def _decode_checks(q, k_pool, v_pool, block_table, seq_lens, workspace, out=None):
+    tensors = dict(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
+                   seq_lens=seq_lens, workspace=workspace)
+    if out is not None:
+        tensors["out"] = out
+    _check_device_tensors(**tensors)
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _require(t.dtype == torch.bfloat16, f"{name} must be bfloat16")
+    _require(out is None or (out.dtype == torch.bfloat16 and out.shape == q.shape),
+             "out must be bfloat16 with q's shape")
+    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+             "block_table and seq_lens must be int32")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape, "k_pool/v_pool: [P, ps, Hkv, d]")
+    _require(q.dim() == 3 and q.shape[2] == k_pool.shape[3], "q: [batch, Hq, d]")
+    _require(seq_lens.numel() == q.shape[0] and block_table.shape[0] >= q.shape[0],
+             "seq_lens: [batch]; block_table: [batch, maxp]")
+
+
+def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace, stream=None):
+    """One query token per sequence over all its L_b cached tokens (split-KV + combine)."""
+    _decode_checks(q, k_pool, v_pool, block_table, seq_lens, workspace, out)
+    lay = layout_of(k_pool, block_table)
+    st = load_library().pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                  _ptr(seq_lens), float(scale), _ptr(out), q.shape[0], q.shape[1],
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  ctypes.byref(lay), _stream(stream))
+    _check(st)
+    return out
+
+
+def pa_decode_partial(q, k_pool, v_pool, block_table, seq_lens, scale, workspace, stream=None):
+    _decode_checks(q, k_pool, v_pool, block_table, seq_lens, workspace)
+    lay = layout_of(k_pool, block_table)
+    st = load_library().pa_decode_partial(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), float(scale),
+        q.shape[0], q.shape[1], _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(lay), _stream(stream))
+    _check(st)
+
+
+def pa_decode_combine(seq_lens, out, workspace, layout: KVLayout, stream=None):
+    _check_device_tensors(seq_lens=seq_lens, out=out, workspace=workspace)
+    _require(out.dtype == torch.bfloat16 and out.dim() == 3, "out: bf16 [batch, Hq, d]")
+    st = load_library().pa_decode_combine(
+        _ptr(seq_lens), _ptr(out), out.shape[0], out.shape[1], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ctypes.byref(layout), _stream(stream))
+    _check(st)

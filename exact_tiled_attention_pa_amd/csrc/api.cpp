@@ -1,0 +1,261 @@
+// C-ABI layer of libpagedattn: argument validation, workspace layout, grid
+// sizing and kernel launch.  Never allocates, frees or synchronises; never reads
+// device memory.  See include/pagedattn.h for the contract of every entry point.
+
+#include "pagedattn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+int log2_exact(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return (1 << r) == x ? r : -1;
+}
+
+// Validates the pool layout and the head counts shared by every entry point.
+int check_layout(const pa_kv_layout* layout, int32_t num_q_heads) {
+  if (!layout) return fail(PA_ERR_NULL, "layout is NULL");
+  if (layout->num_pages < 1 || layout->page_size < 1 || layout->num_kv_heads < 1 ||
+      layout->head_dim < 1 || layout->max_pages_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARG,
+                "layout fields must be >= 1 (num_pages=%d page_size=%d num_kv_heads=%d "
+                "head_dim=%d max_pages_per_seq=%d)",
+                layout->num_pages, layout->page_size, layout->num_kv_heads, layout->head_dim,
+                layout->max_pages_per_seq);
+  if (num_q_heads < 1 || num_q_heads % layout->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
+                num_q_heads, layout->num_kv_heads);
+  if (layout->head_dim != 64 && layout->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim=%d: supported values are 64 and 128",
+                layout->head_dim);
+  const int lg = log2_exact(layout->page_size);
+  if (lg < 4 || lg > 8)
+    return fail(PA_ERR_UNSUPPORTED, "page_size=%d: must be a power of two in [16, 256]",
+                layout->page_size);
+  if ((int64_t)layout->max_pages_per_seq * layout->page_size > (int64_t)1 << 30)
+    return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size exceeds 2^30 tokens");
+  return PA_OK;
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(PA_ERR_INVALID_ARG, "scale=%g must be finite and >= 0", (double)scale);
+  return PA_OK;
+}
+
+int split_tokens_of(const pa_kv_layout* layout) {
+  return layout->page_size > pa::kDecodeSplitTokens ? layout->page_size
+                                                     : pa::kDecodeSplitTokens;
+}
+
+int max_splits_of(const pa_kv_layout* layout) {
+  const int64_t tokens = (int64_t)layout->max_pages_per_seq * layout->page_size;
+  const int st = split_tokens_of(layout);
+  return (int)((tokens + st - 1) / st);
+}
+
+// Workspace: fp32 O partials first, then (m, l) pairs, each region 256-byte aligned.
+size_t ws_o_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
+  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout) * layout->head_dim;
+  return (n * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t ws_ml_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
+  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout) * 2;
+  return (n * sizeof(float) + 255) / 256 * 256;
+}
+
+int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                        const int32_t* block_table, const int32_t* seq_lens, float scale,
+                        int32_t batch, int32_t num_q_heads, const void* workspace,
+                        size_t workspace_bytes, const pa_kv_layout* layout, bool need_inputs) {
+  int st = check_layout(layout, num_q_heads);
+  if (st) return st;
+  if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch=%d must be >= 0", batch);
+  if (batch > 65535) return fail(PA_ERR_INVALID_ARG, "batch=%d exceeds 65535", batch);
+  if (need_inputs) {
+    if (!q || !k_pool || !v_pool || !block_table)
+      return fail(PA_ERR_NULL, "q, k_pool, v_pool and block_table must be non-NULL");
+    st = check_scale(scale);
+    if (st) return st;
+  }
+  if (!seq_lens) return fail(PA_ERR_NULL, "seq_lens must be non-NULL");
+  const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is too small (need %zu)",
+                workspace_bytes, need);
+  return PA_OK;
+}
+
+pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                           const int32_t* block_table, const int32_t* seq_lens, float scale,
+                           pa_bf16* out, int32_t batch, int32_t num_q_heads,
+                           const void* workspace, const pa_kv_layout* layout) {
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + ws_o_bytes(batch, num_q_heads, layout));
+  a.scale = scale;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = layout->num_kv_heads;
+  a.head_dim = layout->head_dim;
+  a.log2_page_size = log2_exact(layout->page_size);
+  a.max_pages_per_seq = layout->max_pages_per_seq;
+  a.split_tokens = split_tokens_of(layout);
+  a.max_splits = max_splits_of(layout);
+  return a;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+               const int32_t* block_table, const int32_t* seq_lens, int causal, float scale,
+               pa_bf16* out, const int32_t* q_start, int32_t batch, int32_t num_q_heads,
+               int32_t max_q_len, const pa_kv_layout* layout, hipStream_t stream) {
+  int st = check_layout(layout, num_q_heads);
+  if (st) return st;
+  if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch=%d must be >= 0", batch);
+  if (batch > 65535) return fail(PA_ERR_INVALID_ARG, "batch=%d exceeds 65535", batch);
+  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len=%d must be >= 0", max_q_len);
+  if ((int64_t)max_q_len > (int64_t)layout->max_pages_per_seq * layout->page_size)
+    return fail(PA_ERR_INVALID_ARG,
+                "max_q_len=%d exceeds the table's capacity of %lld tokens per sequence",
+                max_q_len, (long long)layout->max_pages_per_seq * layout->page_size);
+  if (num_q_heads > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads=%d exceeds 65535", num_q_heads);
+  if ((max_q_len + pa::kPrefillBlockM - 1) / pa::kPrefillBlockM > 65535)
+    return fail(PA_ERR_INVALID_ARG, "max_q_len=%d needs more than 65535 query tiles", max_q_len);
+  st = check_scale(scale);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out || !q_start)
+    return fail(PA_ERR_NULL, "every array argument of pa_prefill must be non-NULL");
+  if (batch == 0 || max_q_len == 0) return ok();
+
+  pa::PrefillArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.q_start = q_start;
+  a.out = out;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = layout->num_kv_heads;
+  a.head_dim = layout->head_dim;
+  a.log2_page_size = log2_exact(layout->page_size);
+  a.max_pages_per_seq = layout->max_pages_per_seq;
+  a.max_q_len = max_q_len;
+  return hip_status(pa::launch_prefill(a, stream), "prefill launch");
+}
+
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                 const pa_kv_layout* layout) {
+  if (check_layout(layout, num_q_heads) != PA_OK || batch < 0) return 0;
+  return ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
+}
+
+int32_t pa_decode_split_tokens(const pa_kv_layout* layout) {
+  if (!layout || log2_exact(layout->page_size) < 4 || log2_exact(layout->page_size) > 8)
+    return 0;
+  return split_tokens_of(layout);
+}
+
+int pa_decode_partial(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, float scale,
+                      int32_t batch, int32_t num_q_heads, void* workspace,
+                      size_t workspace_bytes, const pa_kv_layout* layout, hipStream_t stream) {
+  int st = check_decode_common(q, k_pool, v_pool, block_table, seq_lens, scale, batch,
+                               num_q_heads, workspace, workspace_bytes, layout, true);
+  if (st) return st;
+  if (batch == 0) return ok();
+  const pa::DecodeArgs a = decode_args(q, k_pool, v_pool, block_table, seq_lens, scale,
+                                       nullptr, batch, num_q_heads, workspace, layout);
+  return hip_status(pa::launch_decode_partial(a, stream), "decode partial launch");
+}
+
+int pa_decode_combine(const int32_t* seq_lens, pa_bf16* out, int32_t batch,
+                      int32_t num_q_heads, const void* workspace, size_t workspace_bytes,
+                      const pa_kv_layout* layout, hipStream_t stream) {
+  int st = check_decode_common(nullptr, nullptr, nullptr, nullptr, seq_lens, 1.f, batch,
+                               num_q_heads, workspace, workspace_bytes, layout, false);
+  if (st) return st;
+  if (!out) return fail(PA_ERR_NULL, "out must be non-NULL");
+  if (batch == 0) return ok();
+  const pa::DecodeArgs a = decode_args(nullptr, nullptr, nullptr, nullptr, seq_lens, 1.f, out,
+                                       batch, num_q_heads, workspace, layout);
+  return hip_status(pa::launch_decode_combine(a, stream), "decode combine launch");
+}
+
+int pa_decode(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+              const int32_t* block_table, const int32_t* seq_lens, float scale, pa_bf16* out,
+              int32_t batch, int32_t num_q_heads, void* workspace, size_t workspace_bytes,
+              const pa_kv_layout* layout, hipStream_t stream) {
+  int st = check_decode_common(q, k_pool, v_pool, block_table, seq_lens, scale, batch,
+                               num_q_heads, workspace, workspace_bytes, layout, true);
+  if (st) return st;
+  if (!out) return fail(PA_ERR_NULL, "out must be non-NULL");
+  if (batch == 0) return ok();
+  const pa::DecodeArgs a = decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, out,
+                                       batch, num_q_heads, workspace, layout);
+  st = hip_status(pa::launch_decode_partial(a, stream), "decode partial launch");
+  if (st) return st;
+  return hip_status(pa::launch_decode_combine(a, stream), "decode combine launch");
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: a size or scalar is out of range";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim or page_size not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: decode workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown pa_status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+const char* pa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

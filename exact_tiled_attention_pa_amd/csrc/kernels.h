@@ -1,0 +1,61 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  uint16_t* out;
+  float scale;
+  int causal;
+  int batch;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;
+  int log2_page_size;
+  int max_pages_per_seq;
+  int max_q_len;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  uint16_t* out;
+  float* ws_o;        // [batch, num_q_heads, max_splits, head_dim]
+  float* ws_ml;       // [batch, num_q_heads, max_splits, 2]  (m in log2 units, l)
+  float scale;
+  int batch;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;
+  int log2_page_size;
+  int max_pages_per_seq;
+  int split_tokens;
+  int max_splits;
+};
+
+// Rows of queries per prefill workgroup (4 waves x 32 rows) and keys per tile.
+constexpr int kPrefillBlockM = 128;
+constexpr int kPrefillBlockN = 64;
+
+// Keys per decode split when pages are at most this long.
+constexpr int kDecodeSplitTokens = 512;
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pa

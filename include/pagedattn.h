@@ -1,0 +1,176 @@
+/*
+ * libpagedattn: exact attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * Computes O = softmax(scale * Q K^T) V exactly (up to floating-point rounding)
+ * in the FlashAttention manner: K/V tiles are staged on chip, a running row
+ * max and row sum implement an online softmax, and the score / probability
+ * matrices are never written to device memory.  K and V are read in place from
+ * a paged pool through a per-sequence block table.
+ *
+ * Sources, cited by page title and section:
+ *   [FA-PA]  "FlashAttention and PagedAttention: Two Fixes for Two Different
+ *            Bottlenecks": "Why attention is costly" (the formula), "How it works"
+ *            under FlashAttention (tiling, online softmax, fusion) and under
+ *            PagedAttention (fixed-size blocks, block table, a kernel that reads
+ *            the scattered blocks), "In code" (causal flag, token-major layout).
+ *   [PFA]    "What is Paged FlashAttention?": "How does it work?" (locate pages,
+ *            load K/V tiles, online softmax, accumulate) and "Practical example"
+ *            (logical = pos / page_size, offset = pos % page_size,
+ *            physical = block_table[logical]).
+ *   [FA-LLM] "Flash Attention: Fast, Memory-Efficient Attention for LLMs":
+ *            "The Algorithm" (running max / sum, per-tile rescale, final division),
+ *            "Flash Attention 2" (causal tile skipping), "KV Cache" (decode appends
+ *            the new token, then attends over the cache), "Attention Variants"
+ *            (grouped K/V heads).
+ *
+ * Conventions for every entry point
+ *   - bf16 values are passed as raw 16-bit patterns (pa_bf16).  Arithmetic is
+ *     fp32 (MFMA accumulation, fp32 softmax state); outputs are rounded to
+ *     bf16 round-to-nearest-even.
+ *   - All array arguments are device pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; work is enqueued asynchronously on
+ *     the given HIP stream (0 = the null stream).
+ *   - Layouts are row-major:
+ *       q, out          [tokens, num_q_heads, head_dim]
+ *       k_pool, v_pool  [num_pages, page_size, num_kv_heads, head_dim]
+ *       block_table     int32 [batch, max_pages_per_seq]
+ *   - Return value: PA_OK or an error status.  On error nothing is enqueued
+ *     and pa_last_error() describes the cause (thread-local).  No call aborts
+ *     or throws.
+ *   - Device-array contract (not checked on the host, which never reads device
+ *     memory): for sequence b with KV length L_b,
+ *       0 <= block_table[b, p] < num_pages for p < ceil(L_b / page_size);
+ *       table entries past that are never read (any value, e.g. -1);
+ *       L_b <= max_pages_per_seq * page_size.
+ *     Pool slots past L_b (the tail of the last page) and unused pages may hold
+ *     anything, NaN included: they never influence the output.
+ *   - Aliased physical pages (several sequences listing the same page, as with
+ *     shared prefixes) are allowed: pools are only read.  out must not overlap
+ *     any input.
+ *   - Thread-safe: no global mutable state other than the thread-local error text.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pa_bf16; /* raw bf16 bits */
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,          /* a required pointer is NULL */
+  PA_ERR_INVALID_ARG = 2,   /* a size or scalar is out of range */
+  PA_ERR_UNSUPPORTED = 3,   /* valid but not implemented (head_dim, page_size) */
+  PA_ERR_WORKSPACE = 4,     /* decode workspace missing or too small */
+  PA_ERR_HIP = 5            /* the HIP runtime reported an error at launch */
+};
+
+/* Shape of the paged KV pools.  Shared by K and V. */
+typedef struct pa_kv_layout {
+  int32_t num_pages;          /* physical pages in each pool, >= 1 */
+  int32_t page_size;          /* tokens per page: a power of two in [16, 256] */
+  int32_t num_kv_heads;       /* heads stored per token in the pools, >= 1 */
+  int32_t head_dim;           /* 64 or 128 */
+  int32_t max_pages_per_seq;  /* row length (int32 elements) of block_table, >= 1 */
+} pa_kv_layout;
+
+/*
+ * pa_prefill -- attention of a chunk of query rows per sequence over that
+ * sequence's paged keys and values ([FA-LLM] "The Algorithm"; [PFA] "How does it
+ * work?").  Also serves chunked prefill on top of an existing cache.
+ *
+ *   q            [q_start[batch], num_q_heads, head_dim] bf16; rows of sequence b
+ *                are q_start[b] .. q_start[b+1]-1
+ *   k_pool, v_pool  pools described by layout
+ *   block_table  int32 [batch, layout->max_pages_per_seq]
+ *   seq_lens     int32 [batch]: L_b, KV length of sequence b including this chunk
+ *   causal       nonzero: query row i of a chunk of q_len_b rows sits at absolute
+ *                position L_b - q_len_b + i and sees keys 0..that position
+ *                (bottom-right alignment); zero: every row sees keys 0..L_b-1
+ *   scale        multiplies Q K^T; finite and >= 0 (1/sqrt(head_dim) in the usual case)
+ *   out          [q_start[batch], num_q_heads, head_dim] bf16
+ *   q_start      int32 [batch + 1], non-decreasing, q_start[0] = 0; each
+ *                q_len_b = q_start[b+1] - q_start[b] must satisfy q_len_b <= L_b
+ *   batch        number of sequences, >= 0 (0: nothing to do)
+ *   num_q_heads  multiple of layout->num_kv_heads; query head h reads KV head
+ *                h / (num_q_heads / num_kv_heads)
+ *   max_q_len    host-side upper bound of every q_len_b (sizes the grid without
+ *                reading device memory); rows past q_len_b are never written
+ * Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG (sizes, scale, max_q_len above
+ * max_pages_per_seq * page_size), PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ */
+int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+               const int32_t* block_table, const int32_t* seq_lens, int causal,
+               float scale, pa_bf16* out, const int32_t* q_start, int32_t batch,
+               int32_t num_q_heads, int32_t max_q_len, const pa_kv_layout* layout,
+               hipStream_t stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for `batch` sequences: per
+ * (sequence, query head, split) one partial (m, l, O[head_dim]) in fp32.
+ * Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                 const pa_kv_layout* layout);
+
+/* Key positions covered by one decode split (a multiple of page_size). */
+int32_t pa_decode_split_tokens(const pa_kv_layout* layout);
+
+/*
+ * pa_decode -- one new query token per sequence attending over all L_b cached
+ * tokens of its sequence, the new token included ([FA-LLM] "KV Cache": the new
+ * K_t, V_t are appended before attending).  Memory-bound: each sequence's pages
+ * are split into ranges handled by separate workgroups, whose partial
+ * (row max, row sum, unnormalised output) triples are merged by a second pass
+ * with the same rescaling algebra as the online softmax ([FA-LLM] "The Algorithm").
+ *
+ *   q         [batch, num_q_heads, head_dim] bf16
+ *   seq_lens  int32 [batch], each L_b >= 1 (a sequence with L_b = 0 gets zeros)
+ *   scale     finite and >= 0
+ *   out       [batch, num_q_heads, head_dim] bf16
+ *   workspace device buffer of at least pa_decode_workspace_bytes(...) bytes,
+ *             any contents; calls that share a workspace must be ordered on
+ *             one stream
+ * Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
+ * PA_ERR_HIP.
+ */
+int pa_decode(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+              const int32_t* block_table, const int32_t* seq_lens, float scale,
+              pa_bf16* out, int32_t batch, int32_t num_q_heads, void* workspace,
+              size_t workspace_bytes, const pa_kv_layout* layout, hipStream_t stream);
+
+/*
+ * The two passes of pa_decode as separate calls, for callers that interleave
+ * other work between them or time them separately.  pa_decode(...) is exactly
+ * pa_decode_partial(...) followed by pa_decode_combine(...) on the same stream
+ * with the same arguments.
+ */
+int pa_decode_partial(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, float scale,
+                      int32_t batch, int32_t num_q_heads, void* workspace,
+                      size_t workspace_bytes, const pa_kv_layout* layout,
+                      hipStream_t stream);
+int pa_decode_combine(const int32_t* seq_lens, pa_bf16* out, int32_t batch,
+                      int32_t num_q_heads, const void* workspace, size_t workspace_bytes,
+                      const pa_kv_layout* layout, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

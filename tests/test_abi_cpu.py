@@ -1,0 +1,123 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header declares,
+and rejects bad arguments with the documented status before touching the GPU
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_pa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pa_version().decode().count(".") == 2
+    for st in range(6):
+        assert lib.pa_status_string(st).decode().startswith("PA_")
+    assert "unknown" in lib.pa_status_string(99).decode()
+
+
+def lay(num_pages=12, ps=256, hkv=1, d=64, maxp=3):
+    return B.make_layout(num_pages, ps, hkv, d, maxp)
+
+
+def prefill(lib, layout, *, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, causal=1, scale=0.125,
+            out=FAKE, qs=FAKE, batch=1, hq=1, max_q_len=600):
+    return lib.pa_prefill(q, k, v, bt, lens, causal, scale, out, qs, batch, hq, max_q_len,
+                          ctypes.byref(layout), None)
+
+
+@pytest.mark.parametrize("kw,layout_kw,status", [
+    (dict(q=None), {}, B.PA_ERR_NULL),
+    (dict(out=None), {}, B.PA_ERR_NULL),
+    (dict(qs=None), {}, B.PA_ERR_NULL),
+    ({}, dict(d=96), B.PA_ERR_UNSUPPORTED),
+    ({}, dict(ps=8), B.PA_ERR_UNSUPPORTED),
+    ({}, dict(ps=512), B.PA_ERR_UNSUPPORTED),
+    ({}, dict(ps=48), B.PA_ERR_UNSUPPORTED),
+    ({}, dict(num_pages=0), B.PA_ERR_INVALID_ARG),
+    (dict(batch=-1), {}, B.PA_ERR_INVALID_ARG),
+    (dict(hq=3), dict(hkv=2), B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), {}, B.PA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), {}, B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), {}, B.PA_ERR_INVALID_ARG),
+    (dict(max_q_len=769), {}, B.PA_ERR_INVALID_ARG),   # 3 pages of 256 hold 768 tokens
+    (dict(max_q_len=-5), {}, B.PA_ERR_INVALID_ARG),
+])
+def test_prefill_rejects(lib, kw, layout_kw, status):
+    st = prefill(lib, lay(**layout_kw), **kw)
+    assert st == status, (st, B.last_error())
+    assert B.last_error()
+
+
+def test_prefill_empty_batch_is_ok_without_device(lib):
+    assert prefill(lib, lay(), batch=0) == B.PA_OK
+    assert prefill(lib, lay(), max_q_len=0) == B.PA_OK
+    assert B.last_error() == ""
+
+
+def test_decode_workspace_size_formula(lib):
+    layout = B.make_layout(17000, 16, 32, 128, 512)
+    # 512 pages x 16 tokens, 512-token splits -> 16 splits per sequence
+    assert lib.pa_decode_split_tokens(ctypes.byref(layout)) == 512
+    o = 64 * 32 * 16 * 128 * 4
+    ml = 64 * 32 * 16 * 2 * 4
+    r = lambda n: (n + 255) // 256 * 256
+    assert lib.pa_decode_workspace_bytes(64, 32, ctypes.byref(layout)) == r(o) + r(ml)
+    big = B.make_layout(128, 256, 8, 128, 128)
+    assert lib.pa_decode_split_tokens(ctypes.byref(big)) == 512
+    bad = B.make_layout(128, 24, 8, 128, 128)
+    assert lib.pa_decode_workspace_bytes(1, 8, ctypes.byref(bad)) == 0
+
+
+def test_decode_rejects(lib):
+    layout = B.make_layout(100, 16, 4, 128, 10)
+    need = lib.pa_decode_workspace_bytes(2, 4, ctypes.byref(layout))
+    call = lambda **kw: lib.pa_decode(
+        kw.get("q", FAKE), FAKE, FAKE, FAKE, kw.get("lens", FAKE), kw.get("scale", 0.1),
+        kw.get("out", FAKE), kw.get("batch", 2), kw.get("hq", 4), kw.get("ws", FAKE),
+        kw.get("ws_bytes", need), ctypes.byref(kw.get("layout", layout)), None)
+    assert call(q=None) == B.PA_ERR_NULL
+    assert call(out=None) == B.PA_ERR_NULL
+    assert call(lens=None) == B.PA_ERR_NULL
+    assert call(ws=None) == B.PA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == B.PA_ERR_WORKSPACE
+    assert call(scale=float("nan")) == B.PA_ERR_INVALID_ARG
+    assert call(hq=6) == B.PA_ERR_INVALID_ARG
+    assert call(layout=B.make_layout(100, 16, 4, 80, 10)) == B.PA_ERR_UNSUPPORTED
+    assert call(batch=0) == B.PA_OK
+    st = lib.pa_decode_partial(FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 2, 4, None, need,
+                               ctypes.byref(layout), None)
+    assert st == B.PA_ERR_WORKSPACE
+    st = lib.pa_decode_combine(FAKE, None, 2, 4, FAKE, need, ctypes.byref(layout), None)
+    assert st == B.PA_ERR_NULL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.pa_prefill(q, q, q, q, q, True, 0.1, q, q, 4)

@@ -1,0 +1,344 @@
+"""GPU parity: the HIP library (called through the C ABI) against the fp64 oracle on
+identical seeded inputs.  Bar: max |O_gpu - O_ref| <= 1e-2 and mean <= 1e-3; the
+block-table address math bit-exact (address probe, permutation invariance)."""
+import numpy as np
+import pytest
+import torch
+
+from exact_tiled_attention_pa_amd import binding as B
+from exact_tiled_attention_pa_amd import workloads as W
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    G.gpu_or_skip()
+
+
+# ----------------------------------------------------------------- small, element-wise
+
+def test_prefill_600_worked_example_full():
+    """Paged causal prefill on the worked example's layout (600 tokens, pages of 256,
+    table [5, 1, 9]); unread slots hold NaN.  Every output element is compared."""
+    G.banner("prefill_600 full, poisoned pool")
+    wl = W.prefill_600(device="cuda", poison=True)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), "prefill_600")
+
+
+PREFILL_CASES = [
+    # (head_dim, page_size, causal, Hq, Hkv, lens, q_lens)
+    (128, 16, True, 4, 4, [1, 200, 777], [1, 200, 300]),
+    (128, 16, False, 4, 4, [1, 200, 777], [1, 200, 300]),
+    (128, 256, True, 2, 2, [64, 1000], [64, 129]),
+    (128, 32, True, 8, 2, [300, 513], [300, 17]),
+    (128, 64, False, 4, 1, [129, 65], [129, 65]),
+    (64, 16, True, 3, 3, [259, 31], [259, 31]),
+    (64, 128, False, 2, 2, [1000, 1], [999, 1]),
+    (64, 256, True, 4, 2, [700], [700]),
+]
+
+
+@pytest.mark.parametrize("d,ps,causal,hq,hkv,lens,q_lens", PREFILL_CASES)
+def test_prefill_small_element_wise(d, ps, causal, hq, hkv, lens, q_lens):
+    G.banner(f"prefill small d={d} ps={ps} causal={causal} Hq={hq} Hkv={hkv} lens={lens} "
+             f"q_lens={q_lens}")
+    wl = W.build("small", 100 + d + ps, heads=hkv, head_dim=d, page_size=ps, lens=lens,
+                 q_lens=q_lens, causal=causal, kind="prefill", pool_slack=1.3, device="cuda",
+                 poison=True)
+    call = wl.calls[0]
+    if hq != hkv:  # grouped heads: more query heads than K/V heads
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        call.q = (torch.randn(call.q.shape[0], hq, d, generator=gen, device="cuda")
+                  .to(torch.bfloat16))
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    ref = oracle_grouped(wl, call, hq, hkv)
+    G.compare(G.bf16_out_to_f64(out), ref, f"prefill d={d} ps={ps} causal={causal}")
+
+
+def oracle_grouped(wl, call, hq, hkv):
+    """Oracle for grouped heads: query head h reads K/V head h // (hq // hkv); the
+    oracle itself is per-head MHA, so K/V heads are repeated on the host."""
+    if hq == hkv:
+        return G.oracle_for(wl, call)
+    from oracle import attention as OA
+    seqs = list(range(call.batch))
+    q, k, v, table = G.host_inputs(wl, call, seqs)
+    rep = hq // hkv
+    k = np.repeat(k, rep, axis=2)
+    v = np.repeat(v, rep, axis=2)
+    if call.kind == "prefill":
+        ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host,
+                                  call.causal, wl.scale)
+    else:
+        ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale)
+    return ref
+
+
+DECODE_CASES = [
+    # (head_dim, page_size, Hq, Hkv, lens)
+    (128, 16, 4, 4, [1, 15, 16, 17, 511, 512, 513, 3000]),
+    (128, 256, 2, 2, [1, 255, 256, 257, 1500]),
+    (64, 16, 3, 3, [7, 1024, 2049]),
+    (128, 32, 8, 2, [100, 700]),
+    (64, 64, 4, 1, [65, 1]),
+]
+
+
+@pytest.mark.parametrize("d,ps,hq,hkv,lens", DECODE_CASES)
+def test_decode_small_element_wise(d, ps, hq, hkv, lens):
+    G.banner(f"decode small d={d} ps={ps} Hq={hq} Hkv={hkv} lens={lens}")
+    wl = W.build("small", 200 + d + ps, heads=hkv, head_dim=d, page_size=ps, lens=lens,
+                 kind="decode", pool_slack=1.2, device="cuda", poison=True)
+    call = wl.calls[0]
+    if hq != hkv:
+        gen = torch.Generator(device="cuda").manual_seed(9)
+        call.q = torch.randn(len(lens), hq, d, generator=gen, device="cuda").to(torch.bfloat16)
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), oracle_grouped(wl, call, hq, hkv),
+              f"decode d={d} ps={ps}")
+
+
+def test_decode_two_passes_equal_one_call():
+    G.banner("decode partial+combine vs pa_decode")
+    wl = W.build("small", 5, heads=4, head_dim=128, page_size=16, lens=[40, 1300, 900],
+                 kind="decode", device="cuda", poison=True)
+    call = wl.calls[0]
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    one = G.run_call(wl, call, workspace=ws)
+    two = torch.empty_like(one)
+    B.pa_decode_partial(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
+                        wl.scale, ws)
+    B.pa_decode_combine(call.seq_lens, two, ws, B.layout_of(wl.k_pool, call.block_table))
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+
+
+# ----------------------------------------------------------------- full-size, sampled
+
+def test_decode_64_sampled():
+    G.banner("decode_64 full size, 8 sequences sampled (all heads)")
+    wl = W.decode_64(device="cuda", poison=True)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    lens = call.seq_lens_host
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 17, 31, 42, 50})
+    ref = G.oracle_for(wl, call, seqs=seqs)
+    G.compare(G.bf16_out_to_f64(out), ref, "decode_64")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_4096_sampled(causal):
+    G.banner(f"prefill_4096 causal={causal} full size, rows sampled (all heads)")
+    wl = W.prefill_4096(device="cuda", poison=True, causal=causal)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    rows = {0: G.spread_rows(4096, 48, seed=1)}
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, rows=rows),
+              f"prefill_4096 causal={causal}")
+
+
+def test_prefill_32k_sampled():
+    G.banner("prefill_32k full size, rows sampled (all heads)")
+    wl = W.prefill_32k(device="cuda", poison=True)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    rows = {0: G.spread_rows(32768, 40, seed=2, tile=4096)}
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, rows=rows), "prefill_32k")
+
+
+def test_mixed_128x4_sampled():
+    G.banner("mixed_128x4 full size: decode then chunked prefill on one stream, sampled")
+    wl = W.mixed_128x4(device="cuda", poison=True)
+    dec, pre = wl.calls
+    out_d = G.run_call(wl, dec)
+    out_p = G.run_call(wl, pre)
+    torch.cuda.synchronize()
+    lens = dec.seq_lens_host
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 127, 64})
+    G.compare(G.bf16_out_to_f64(out_d), G.oracle_for(wl, dec, seqs=seqs), "mixed decode")
+    rows = {b: G.spread_rows(2048, 12, seed=10 + b) for b in range(4)}
+    G.compare(G.bf16_out_to_f64(out_p), G.oracle_for(wl, pre, rows=rows), "mixed chunks")
+
+
+# ----------------------------------------------------------------- address math, bit-exact
+
+def _encode_slots(wl):
+    """V[p, o, h, :] := (p % 128, (p // 128) % 128, p // 16384, o, h, 0, ...): small
+    integers, exact in bf16, that name the slot they sit in."""
+    P, ps, H, d = wl.v_pool.shape
+    dev = wl.v_pool.device
+    p = torch.arange(P, device=dev, dtype=torch.float32)[:, None, None]
+    o = torch.arange(ps, device=dev, dtype=torch.float32)[None, :, None]
+    h = torch.arange(H, device=dev, dtype=torch.float32)[None, None, :]
+    enc = torch.zeros(P, ps, H, d, device=dev, dtype=torch.float32)
+    enc[..., 0] = (p % 128).expand(P, ps, H)
+    enc[..., 1] = ((p // 128) % 128).expand(P, ps, H)
+    enc[..., 2] = (p // 16384).expand(P, ps, H)
+    enc[..., 3] = o.expand(P, ps, H)
+    enc[..., 4] = h.expand(P, ps, H)
+    wl.v_pool.copy_(enc.to(torch.bfloat16))
+
+
+def _decode_slot(row: torch.Tensor):
+    """Inverse of _encode_slots for output rows [..., d] -> (page, offset, head)."""
+    r = row.float()
+    page = r[..., 0] + 128 * r[..., 1] + 16384 * r[..., 2]
+    return page.long(), r[..., 3].long(), r[..., 4].long()
+
+
+def test_address_probe_decode():
+    """Each sequence's query aligns with one spike key (margin ~260 in log2 units, so
+    every other weight is exactly 0 in fp32): the output must be, bit for bit, the
+    V row of the slot the block table names for that token."""
+    G.banner("address probe, decode_64 layout")
+    wl = W.decode_64(device="cuda")
+    call = wl.calls[0]
+    H, d, ps = wl.heads, wl.head_dim, wl.page_size
+    wl.k_pool.zero_()
+    _encode_slots(wl)
+    rng = np.random.default_rng(3)
+    lens = call.seq_lens_host
+    q = torch.zeros(call.batch, H, d, device="cuda", dtype=torch.bfloat16)
+    want = []
+    for b in range(call.batch):
+        t = int(rng.integers(0, lens[b])) if b % 3 else int(lens[b] - 1 - b % 2)
+        phys = int(call.block_table_host[b, t // ps])
+        wl.k_pool[phys, t % ps, :, 5] = 64.0
+        q[b, :, 5] = 32.0
+        want.append((phys, t % ps))
+        # the spike channel of every other sequence is different (channel 5 vs none)
+    call.q = q
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    page, off, head = _decode_slot(out)
+    for b, (phys, o) in enumerate(want):
+        assert torch.all(page[b] == phys) and torch.all(off[b] == o), (b, phys, o)
+        assert torch.equal(head[b].cpu(), torch.arange(H))
+
+
+def test_address_probe_prefill_paged():
+    """Causal paged prefill on the 32k layout (shuffled pages of 256): 64 target tokens
+    spread over every page, each on its own key channel; every sampled query row aligns
+    with one visible target and must return that slot's V row exactly."""
+    G.banner("address probe, prefill_32k layout")
+    wl = W.prefill_32k(device="cuda")
+    call = wl.calls[0]
+    H, d, ps = wl.heads, wl.head_dim, wl.page_size
+    wl.k_pool.zero_()
+    _encode_slots(wl)
+    rng = np.random.default_rng(4)
+    L = 32768
+    targets = np.sort(rng.choice(L, size=64, replace=False))
+    targets[0] = 0
+    q = torch.zeros(L, H, d, device="cuda", dtype=torch.bfloat16)
+    slot_of = {}
+    for c, t in enumerate(targets):
+        phys = int(call.block_table_host[0, t // ps])
+        wl.k_pool[phys, t % ps, :, c] = 64.0
+        slot_of[c] = (phys, int(t % ps))
+    rows = rng.choice(L, size=4096, replace=False)
+    chan = np.empty(len(rows), dtype=np.int64)
+    for i, r in enumerate(rows):
+        visible = np.nonzero(targets <= r)[0]
+        chan[i] = visible[rng.integers(0, len(visible))]
+        q[int(r), :, int(chan[i])] = 32.0
+    call.q = q
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    page, off, _ = _decode_slot(out[torch.as_tensor(rows, device="cuda")])
+    want_p = torch.tensor([slot_of[int(c)][0] for c in chan], device="cuda")
+    want_o = torch.tensor([slot_of[int(c)][1] for c in chan], device="cuda")
+    assert torch.all(page == want_p[:, None]) and torch.all(off == want_o[:, None])
+
+
+def _permute_pages(wl, calls, seed):
+    P = wl.k_pool.shape[0]
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    sigma = torch.randperm(P, generator=g)
+    k2 = torch.empty_like(wl.k_pool)
+    v2 = torch.empty_like(wl.v_pool)
+    k2[sigma.cuda()] = wl.k_pool
+    v2[sigma.cuda()] = wl.v_pool
+    tables = []
+    for c in calls:
+        t = c.block_table.long()
+        tables.append(torch.where(t >= 0, sigma.cuda()[t.clamp(min=0)], t).to(torch.int32))
+    return k2, v2, tables
+
+
+@pytest.mark.parametrize("which", ["decode_64", "prefill_32k"])
+def test_permuting_physical_pages_is_bitwise_invariant(which):
+    """Relabelling physical pages (moving them in the pool and remapping the table)
+    must not change a single output bit: the kernels visit keys in logical order."""
+    G.banner(f"page permutation invariance, {which}")
+    wl = W.FULL_WORKLOADS[which](device="cuda", poison=True)
+    call = wl.calls[0]
+    base = G.run_call(wl, call)
+    k2, v2, (t2,) = _permute_pages(wl, [call], seed=99)
+    out = torch.empty_like(base)
+    if call.kind == "prefill":
+        B.pa_prefill(call.q, k2, v2, t2, call.seq_lens, call.causal, wl.scale, out,
+                     call.q_start, call.max_q_len)
+    else:
+        ws = B.decode_workspace(call.q, k2, t2)
+        B.pa_decode(call.q, k2, v2, t2, call.seq_lens, wl.scale, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(base, out)
+
+
+def test_poisoned_and_clean_pools_agree_bitwise():
+    """NaN in tail slots and unused pages must not change the output."""
+    G.banner("poison vs clean, small prefill + decode")
+    for kind in ("prefill", "decode"):
+        a = W.build("p", 31, heads=2, head_dim=128, page_size=16, lens=[37, 300],
+                    q_lens=[37, 100] if kind == "prefill" else None, kind=kind,
+                    pool_slack=1.5, device="cuda", poison=False)
+        b = W.build("p", 31, heads=2, head_dim=128, page_size=16, lens=[37, 300],
+                    q_lens=[37, 100] if kind == "prefill" else None, kind=kind,
+                    pool_slack=1.5, device="cuda", poison=True)
+        oa = G.run_call(a, a.calls[0])
+        ob = G.run_call(b, b.calls[0])
+        torch.cuda.synchronize()
+        assert torch.isfinite(ob.float()).all()
+        assert torch.equal(oa, ob), kind
+
+
+def test_constant_values_return_the_constant():
+    G.banner("constant V")
+    for kind in ("prefill", "decode"):
+        wl = W.build("c", 41, heads=2, head_dim=128, page_size=16, lens=[1, 500, 64],
+                     q_lens=[1, 500, 10] if kind == "prefill" else None, kind=kind,
+                     device="cuda", poison=True)
+        used = torch.isfinite(wl.v_pool.float())
+        wl.v_pool[used] = 1.75
+        out = G.run_call(wl, wl.calls[0]).float()
+        torch.cuda.synchronize()
+        # within one bf16 ulp of 1.75 (ulp 2^-7 in [1, 2))
+        assert (out - 1.75).abs().max().item() <= 2 ** -7, kind
+
+
+def test_empty_batch_and_zero_rows_are_no_ops():
+    G.banner("empty batch")
+    wl = W.build("e", 1, heads=1, head_dim=64, page_size=16, lens=[5], q_lens=[5],
+                 device="cuda")
+    call = wl.calls[0]
+    out = torch.full_like(call.q, 3.0)
+    lay = B.layout_of(wl.k_pool, call.block_table)
+    lib = B.load_library()
+    import ctypes
+    st = lib.pa_prefill(call.q.data_ptr(), wl.k_pool.data_ptr(), wl.v_pool.data_ptr(),
+                        call.block_table.data_ptr(), call.seq_lens.data_ptr(), 1, wl.scale,
+                        out.data_ptr(), call.q_start.data_ptr(), 0, 1, 5, ctypes.byref(lay),
+                        None)
+    torch.cuda.synchronize()
+    assert st == B.PA_OK and torch.all(out == 3.0)

@@ -17,25 +17,35 @@
 //         positions, skipping tiles entirely in the causal future (same section:
 //         masked future tokens are skipped).
 //
-// Per key tile:
-//   - the tile's physical pages come from the block table (at most 4 pages of 16);
-//     each thread loads its 16-byte pieces of K and V rows into registers one tile
-//     ahead (software pipelining), then writes them to LDS: K row-major, V
-//     transposed (d-major) with key order permuted inside 16-key groups so the
-//     PV MFMA operand of every lane is one 16-byte LDS read;
+// K/V tile staging (no VGPR round trip, no per-element address arithmetic):
+//   - a 64-key tile is 4 groups of 16 keys; a group never straddles a page (pages
+//     hold a power of two >= 16 tokens), so its physical page is one scalar
+//     block-table load and its address one scalar base;
+//   - each wave issues buffer loads straight into LDS (16 B per lane, 1 KB per
+//     instruction) against a buffer resource whose base is the group's first row
+//     and whose size covers only the rows below the sequence length: rows past
+//     the end read as zero, so stale or NaN bytes in a partly filled last page
+//     never reach the MFMAs;
+//   - LDS keeps the natural [key][d] layout with the 16-byte chunks of each row
+//     XOR-swizzled by the row index, so the K reads (ds_read_b128) and the
+//     transposing V reads (ds_read_b64_tr_b16) are free of bank conflicts;
+//   - two LDS stages: tile j+1 streams in while tile j is computed; one barrier
+//     per tile.
+//
+// Per key tile (per wave, 32 query rows):
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q stays in VGPRs for the whole
 //     kernel as the B operand; each lane ends up holding 32 scores of one query
-//     row (its query is lane % 32), so the row statistics are per lane plus one
+//     row (its query is lane % 32), so row statistics are per lane plus one
 //     exchange between lanes l and l ^ 32;
 //   - masking only on tiles that cross the causal diagonal or the sequence end;
-//     pool slots past the end are never loaded (V rows are zero, scores -inf), so
-//     stale or NaN bytes in a partly filled last page cannot leak in;
 //   - online softmax in fp32 with exp2 (scale * log2(e) folded into one FMA).  The
 //     reference max is raised only when a row's max grows by more than 8 (log2
 //     units); the output and row sum always share the same reference, so the
 //     final O / l is unchanged while most tiles skip the rescale of O;
 //   - P rounded to bf16 feeds O^T += V^T P^T, again 32x32x16 MFMA with fp32
-//     accumulators; P never leaves registers.
+//     accumulators; V^T fragments come from the transposing LDS read, whose
+//     4-key x 16-d block per 16 lanes matches the MFMA operand layout, with the
+//     key order of the S^T accumulator registers.
 // Epilogue: O / l, rounded to bf16 (RNE), staged through LDS and written with
 // 16-byte coalesced stores.
 
@@ -46,31 +56,41 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int BM = kPrefillBlockM;  // 128 query rows per workgroup
 constexpr int BN = kPrefillBlockN;  // 64 key positions per tile
 constexpr int kRescaleThreshold = 8;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int D>
-struct PrefillSmem {
-  static constexpr int kStrideK = D + 8;   // bf16 elements per K row (16 B pad)
-  static constexpr int kStrideV = BN + 8;  // bf16 elements per transposed V row
-  static constexpr int kKBytes = BN * kStrideK * 2;
-  static constexpr int kVBytes = D * kStrideV * 2;
-  static constexpr int kOBytes = BM * kStrideK * 2;  // epilogue staging
-  static constexpr int kBytes = (kKBytes + kVBytes) > kOBytes ? (kKBytes + kVBytes) : kOBytes;
+struct Geometry {
+  static constexpr int kRowBytes = 2 * D;                  // one K or V row in LDS
+  static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 1024 / kRowBytes;    // rows per 1 KB load
+  static constexpr int kInstPerWave = BN / kRowsPerInst / kWaves;
+  static constexpr int kTileBytes = BN * kRowBytes;
+  static constexpr int kDK = D / 16;                       // MFMA k-steps over d
+  static constexpr int kDB = D / 32;                       // 32-wide output blocks
+  static constexpr int kStageOut = D + 8;                  // epilogue row stride (elements)
 };
 
-// position inside a 16-key group at which keys 4q .. 4q+3 are stored, so that
-// lanes 0-31 find keys {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15} in one
-// 16-byte read: the key order of a 32x32x16 MFMA output column pair
-__device__ __forceinline__ int vt_group_pos(int q) { return 4 * (((q & 1) << 1) | (q >> 1)); }
+// XOR swizzles of the 16-byte chunks of LDS row r.
+//   K: chunk c of row r sits in slot c ^ (r mod chunks).
+//   V: chunk c of row r sits in slot c ^ v_swizzle(r mod 4).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int r) { return r & (Geometry<D>::kChunks - 1); }
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  const int x = r & 3;
+  return D == 128 ? ((2 * x) ^ (8 * (x & 1))) : 2 * x;
+}
 
-// physical page of the i-th page a key tile touches (i < 4: a 64-key tile spans at
-// most four 16-token pages)
-__device__ __forceinline__ int pick_page(int i, int p0, int p1, int p2, int p3) {
-  const int a = (i & 1) ? p1 : p0;
-  const int b = (i & 1) ? p3 : p2;
-  return (i & 2) ? b : a;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
 }
 
 template <int D, bool CAUSAL>
@@ -80,17 +100,11 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
                const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_start,
                uint16_t* __restrict__ out, float scale_log2, int num_q_heads,
                int num_kv_heads, int log2_ps, int max_pages) {
-  using Smem = PrefillSmem<D>;
-  constexpr int kChunksPerRow = D / 8;         // 16-byte pieces per K/V row
-  constexpr int kKRowsPerPass = kThreads / kChunksPerRow;
-  constexpr int kKLoads = BN / kKRowsPerPass;  // K pieces per thread
-  constexpr int kVThreads = 16 * kChunksPerRow;  // threads that load V (4 keys x 8 d each)
-  constexpr int kDK = D / 16;                  // MFMA k-steps over d
-  constexpr int kDB = D / 32;                  // 32-wide output blocks over d
-
-  __shared__ __attribute__((aligned(16))) char smem[Smem::kBytes];
-  uint16_t* const ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* const vt = reinterpret_cast<uint16_t*>(smem + Smem::kKBytes);
+  using G = Geometry<D>;
+  __shared__ __attribute__((aligned(1024))) char k_lds0[G::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[G::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[G::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[G::kTileBytes];
 
   const int h = blockIdx.x;
   const int b = blockIdx.z;
@@ -104,12 +118,12 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int hk = h / (num_q_heads / num_kv_heads);
   const int ps_mask = (1 << log2_ps) - 1;
-  const size_t token_stride = (size_t)num_kv_heads * D;
+  const int row_bytes_g = num_kv_heads * D * 2;  // token stride in the pools, bytes
   const int32_t* const bt = block_table + (size_t)b * max_pages;
 
   // key range of this workgroup and the first tile that needs a mask
@@ -123,119 +137,94 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
   const int last_page = seq_len > 0 ? (seq_len - 1) >> log2_ps : 0;
 
   // ---- Q fragment (B operand of S^T = K Q^T): row q0 + 32w + lane%32, 8 bf16 per k-step
-  bf16x8 qf[kDK];
+  bf16x8 qf[G::kDK];
   {
     const int r = q0 + wave * 32 + l32;
     if (r < q_len) {
       const uint16_t* src = q + ((size_t)(qs + r) * num_q_heads + h) * D + half * 8;
 #pragma unroll
-      for (int j = 0; j < kDK; ++j)
+      for (int j = 0; j < G::kDK; ++j)
         qf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + j * 16));
     } else {
 #pragma unroll
-      for (int j = 0; j < kDK; ++j) qf[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      for (int j = 0; j < G::kDK; ++j) qf[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
   }
 
-  // ---- register staging of one K/V tile
-  u32x4 kreg[kKLoads];
-  u32x4 vreg[4];
-  const int k_chunk = tid % kChunksPerRow;
-  const int k_row0 = tid / kChunksPerRow;
-  const int v_group = tid % 16;               // keys 4*v_group .. +3 of the tile
-  const int v_chunk = tid / 16;               // d = 8*v_chunk .. +7
-  const bool v_loader = tid < kVThreads;
+  // ---- per-lane constant offsets
+  // Loads: instruction i of wave w fills LDS rows kRowsPerInst*(4i + w) + lane/chunks,
+  // slot lane%chunks.  Those rows sit at the same offset inside their 16-row group for
+  // every i, and have the same swizzle, so one byte offset per lane serves all loads.
+  const int ld_row0 = G::kRowsPerInst * wave + lane / G::kChunks;  // row for i = 0
+  const int ld_row_in_group = ld_row0 & 15;
+  const int ld_slot = lane % G::kChunks;
+  const int k_voff = ld_row_in_group * row_bytes_g + hk * D * 2 +
+                     (ld_slot ^ k_swizzle<D>(ld_row0)) * 16;
+  const int v_voff = ld_row_in_group * row_bytes_g + hk * D * 2 +
+                     (ld_slot ^ v_swizzle<D>(ld_row0)) * 16;
+  // K reads: row 32kb + lane%32, chunk 2jj + half
+  int k_rd[G::kDK];
+#pragma unroll
+  for (int jj = 0; jj < G::kDK; ++jj)
+    k_rd[jj] = l32 * G::kRowBytes + ((2 * jj + half) ^ k_swizzle<D>(l32)) * 16;
+  // V reads (transposing): 16-lane group g reads rows 4*half + 8t + (lane%16)/4 of each
+  // 16-key chunk, d columns 32db + 16(g%2) + 4(lane%4) .. +3
+  int v_rd[G::kDB];
+  {
+    const int j16 = lane & 15;
+    const int g = lane >> 4;
+    const int row = 4 * half + j16 / 4;
+#pragma unroll
+    for (int db = 0; db < G::kDB; ++db) {
+      const int ch = 4 * db + 2 * (g & 1) + (j16 & 3) / 2;
+      v_rd[db] = row * G::kRowBytes + (ch ^ v_swizzle<D>(row)) * 16 + 8 * (j16 & 1);
+    }
+  }
 
-  auto load_tile = [&](int j) {
+  // Streams tile j (64 keys from position 64j) of K and V into one LDS stage.
+  auto issue_tile = [&](int j, char* k_dst, char* v_dst) {
     const int kt0 = j * BN;
-    const int lp0 = kt0 >> log2_ps;
-    // physical pages touched by this tile (at most 4 with 16-token pages), clamped to
-    // the sequence's last page so no table entry past it is read
-    const int p0 = bt[min(lp0, last_page)];
-    const int p1 = bt[min(lp0 + 1, last_page)];
-    const int p2 = bt[min(lp0 + 2, last_page)];
-    const int p3 = bt[min(lp0 + 3, last_page)];
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i) {
-      const int t = kt0 + k_row0 + i * kKRowsPerPass;
-      if (t < seq_len) {
-        const int phys = pick_page((t >> log2_ps) - lp0, p0, p1, p2, p3);
-        const size_t off = (((size_t)phys << log2_ps) + (t & ps_mask)) * token_stride +
-                           (size_t)hk * D + k_chunk * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(k_pool + off);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (v_loader) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = kt0 + v_group * 4 + i;
-        if (t < seq_len) {
-          const int phys = pick_page((t >> log2_ps) - lp0, p0, p1, p2, p3);
-          const size_t off = (((size_t)phys << log2_ps) + (t & ps_mask)) * token_stride +
-                             (size_t)hk * D + v_chunk * 8;
-          vreg[i] = *reinterpret_cast<const u32x4*>(v_pool + off);
-        } else {
-          vreg[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < kKLoads; ++i)
-      *reinterpret_cast<u32x4*>(ks + (k_row0 + i * kKRowsPerPass) * Smem::kStrideK +
-                                k_chunk * 8) = kreg[i];
-    if (v_loader) {
-      const int col = (v_group >> 2) * 16 + vt_group_pos(v_group & 3);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = 8*v_chunk + 2w (low halves) and + 2w + 1 (high halves)
-        const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-        const int d = v_chunk * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(vt + d * Smem::kStrideV + col) = u32x2{lo01, lo23};
-        *reinterpret_cast<u32x2*>(vt + (d + 1) * Smem::kStrideV + col) = u32x2{hi01, hi23};
-      }
+    for (int i = 0; i < G::kInstPerWave; ++i) {
+      const int first_row = G::kRowsPerInst * (kWaves * i + wave);
+      const int t0 = kt0 + (first_row & ~15);       // first token of the 16-row group
+      const int phys = bt[min(t0 >> log2_ps, last_page)];
+      const int valid = min(16, seq_len - t0);      // rows of the group below seq_len
+      const int bytes = valid > 0 ? valid * row_bytes_g : 0;
+      const size_t elem =
+          (((size_t)phys << log2_ps) + (t0 & ps_mask)) * (size_t)num_kv_heads * D;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(k_pool + elem, bytes),
+                                               (lds_void*)(k_dst + first_row * G::kRowBytes),
+                                               16, k_voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(v_pool + elem, bytes),
+                                               (lds_void*)(v_dst + first_row * G::kRowBytes),
+                                               16, v_voff, 0, 0, 0);
     }
   };
 
   // ---- per-lane softmax state for query row q0 + 32w + lane%32
-  const int my_pos = shift + q0 + wave * 32 + l32;      // absolute position of this row
+  const int my_pos = shift + q0 + wave * 32 + l32;  // absolute position of this row
   const int wave_last_pos = shift + q0 + wave * 32 + 31;
   float m_ref = -INFINITY;  // reference max (log2 units) of O and l
   float l_part = 0.f;       // this lane's share of the row sum (its 32 keys per tile)
-  f32x16 oacc[kDB];
+  f32x16 oacc[G::kDB];
 #pragma unroll
-  for (int i = 0; i < kDB; ++i)
+  for (int i = 0; i < G::kDB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
 
-  if (n_tiles > 0) load_tile(0);
-
-  for (int j = 0; j < n_tiles; ++j) {
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);
-
+  auto compute_tile = [&](int j, const char* k_src, const char* v_src) {
     const int kt0 = j * BN;
-    if (CAUSAL && kt0 > wave_last_pos) continue;  // whole tile in this wave's future
-
     // S^T (keys x queries) = K Q^T: two 32-key blocks
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      const uint16_t* krow = ks + (kb * 32 + l32) * Smem::kStrideK + half * 8;
 #pragma unroll
-      for (int jj = 0; jj < kDK; ++jj) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + jj * 16));
+      for (int jj = 0; jj < G::kDK; ++jj) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(k_src + kb * 32 * G::kRowBytes + k_rd[jj]));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[jj], sacc[kb], 0, 0, 0);
       }
     }
@@ -267,7 +256,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
       m_ref = m_new;
       l_part *= alpha;
 #pragma unroll
-      for (int i = 0; i < kDB; ++i)
+      for (int i = 0; i < G::kDB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
@@ -277,52 +266,79 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     float lsum = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float x0 = fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + e], scale_log2, -m_ref));
-        const float x1 = fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + e + 1], scale_log2, -m_ref));
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e], scale_log2, -m_ref));
+        const float x1 =
+            fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e + 1], scale_log2, -m_ref));
         lsum += x0 + x1;
-        pb[c][e] = (__bf16)x0;
-        pb[c][e + 1] = (__bf16)x1;
+        w[e] = pack_bf16x2(x0, x1);
       }
+      pb[c] = __builtin_bit_cast(bf16x8, w);
     }
     l_part += lsum;
 
     // O^T (d x queries) += V^T P^T
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      const uint16_t* vrow = vt + (db * 32 + l32) * Smem::kStrideV + half * 8;
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vrow + c * 16));
+      for (int db = 0; db < G::kDB; ++db) {
+        const char* base = v_src + c * 16 * G::kRowBytes + v_rd[db];
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * G::kRowBytes));
+        // keep the whole-vector bit casts: element-wise access to these results is not
+        // reliable with this compiler
+        const u32x2 wl = __builtin_bit_cast(u32x2, lo);
+        const u32x2 wh = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wh[0], wh[1]});
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[db], 0, 0, 0);
       }
     }
+  };
+
+  auto step = [&](int j, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j landed
+    __syncthreads();                     // everyone's loads landed; tile j-1 fully consumed
+    if (j + 1 < n_tiles) issue_tile(j + 1, k_nxt, v_nxt);
+    if (CAUSAL && j * BN > wave_last_pos) return;  // whole tile in this wave's future
+    compute_tile(j, k_cur, v_cur);
+  };
+
+  if (n_tiles > 0) issue_tile(0, k_lds0, v_lds0);
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, k_lds0, v_lds0, k_lds1, v_lds1);
+    if (j + 1 < n_tiles) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
   // ---- epilogue: O / l -> bf16, staged through LDS for coalesced stores
   const float l_row = pair_sum(l_part);
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  uint16_t* const os = reinterpret_cast<uint16_t*>(smem) + wave * 32 * Smem::kStrideK;
+  // one LDS stage buffer per wave holds that wave's 32 output rows
+  static_assert(32 * G::kStageOut * 2 <= G::kTileBytes, "a wave's rows fit in one stage");
+  char* const stage = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+  uint16_t* const os = reinterpret_cast<uint16_t*>(stage);
 #pragma unroll
-  for (int db = 0; db < kDB; ++db)
+  for (int db = 0; db < G::kDB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = db * 32 + g * 8 + half * 4;
       const uint32_t w0 = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
       const uint32_t w1 = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(os + l32 * Smem::kStrideK + d) = u32x2{w0, w1};
+      *reinterpret_cast<u32x2*>(os + l32 * G::kStageOut + d) = u32x2{w0, w1};
     }
   __syncthreads();
-  constexpr int kPieces = 32 * kChunksPerRow;  // 16-byte pieces of this wave's rows
+  constexpr int kPieces = 32 * G::kChunks;  // 16-byte pieces of this wave's rows
 #pragma unroll
   for (int i = lane; i < kPieces; i += 64) {
-    const int r = i / kChunksPerRow;
-    const int cch = i % kChunksPerRow;
+    const int r = i / G::kChunks;
+    const int cch = i % G::kChunks;
     const int qrow = q0 + wave * 32 + r;
     if (qrow < q_len) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(os + r * Smem::kStrideK + cch * 8);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(os + r * G::kStageOut + cch * 8);
       *reinterpret_cast<u32x4*>(out + ((size_t)(qs + qrow) * num_q_heads + h) * D + cch * 8) = v;
     }
   }
@@ -334,8 +350,8 @@ void launch(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, n_qtiles, a.batch);
   hipLaunchKernelGGL((prefill_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a.q,
                      a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.q_start, a.out,
-                     score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads, a.log2_page_size,
-                     a.max_pages_per_seq);
+                     score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
+                     a.log2_page_size, a.max_pages_per_seq);
 }
 
 }  // namespace

@@ -101,6 +101,9 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
     if (st) return st;
   }
   if (!seq_lens) return fail(PA_ERR_NULL, "seq_lens must be non-NULL");
+  if (max_splits_of(layout) > 65535)
+    return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size = %lld needs more than 65535 "
+                "decode splits", (long long)layout->max_pages_per_seq * layout->page_size);
   const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (workspace_bytes < need)

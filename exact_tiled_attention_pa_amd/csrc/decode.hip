@@ -4,28 +4,32 @@
 // Decode reads every cached K/V byte once and does ~1 FLOP per byte, so it is
 // bound by HBM bandwidth, not by math ("What is Paged FlashAttention?",
 // "Does it change the attention result or complexity?": for single-token decoding
-// the cache reads dominate).  The design therefore aims only at keeping enough
-// bytes in flight:
+// the cache reads dominate).  The design therefore aims only at moving bytes the
+// way HBM likes them:
 //
-//   pass 1 (decode_partial_kernel): grid (split, query head, sequence).  A split
-//     is a range of split_tokens key positions (whole pages).  Its 4 waves take
-//     16-token chunks round-robin; a wave reads a chunk's K and V rows straight
-//     into registers (16 B per lane, one 256 B row per 16 lanes at d = 128), with
-//     the next chunk's loads issued before the current chunk is consumed.  The
-//     physical page of each chunk comes from the block table ("What is Paged
-//     FlashAttention?", "Practical example"), fetched for all of the wave's
-//     chunks by one vector load up front.  Dot products run on the VALU and are
-//     summed across the 16 lanes of a row with DPP moves.  Each 16-lane row group
-//     keeps its own online-softmax state (running max m, running sum l, output
-//     accumulator; "Flash Attention: Fast, Memory-Efficient Attention for
-//     LLMs", "The Algorithm"), so the inner loop needs no cross-row exchange; the
-//     16 row-group states of the workgroup are merged once through LDS and the
-//     split's (m, l, unnormalised O) is written to the workspace.
+//   pass 1 (decode_partial_kernel): grid (head group, split, sequence).  A head
+//     group is the heads one wave load covers: 64 lanes x 16 B = 1 KB = one
+//     token's row for 4 consecutive heads at d = 128 (8 at d = 64), contiguous in
+//     the pool's [page, slot, head, d] layout.  Consecutive workgroups are the
+//     head groups of the same key range, so concurrently running workgroups read
+//     adjacent kilobytes of the same token rows (DRAM row locality), instead of
+//     256-byte pieces 8 KB apart.  A split is a range of split_tokens key
+//     positions (whole pages); its keys come in 16-token chunks and each of the 4
+//     waves takes 4 consecutive tokens of every chunk, straight into registers,
+//     two chunks ahead of the one being consumed.  The physical page of every
+//     chunk comes from the block table ("What is Paged FlashAttention?",
+//     "Practical example"), fetched for the whole split by one vector load.
+//     Dot products run on the VALU and are summed over the 16 lanes of a head
+//     with DPP moves; every 16-lane row group keeps its own online-softmax state
+//     (running max m, running sum l, output accumulator; "Flash Attention: Fast,
+//     Memory-Efficient Attention for LLMs", "The Algorithm"), the 4 waves' states
+//     are merged through LDS and the split's (m, l, unnormalised O) goes to the
+//     workspace.
 //   pass 2 (decode_combine_kernel): per (sequence, head), merges the splits'
 //     partials with the same rescaling algebra and writes bf16 O.
 //
-// m is kept in log2 units (scores times scale * log2(e)) so that every
-// exponential is a single v_exp_f32.
+// Query head h reads K/V head h / (num_q_heads / num_kv_heads).  m is kept in
+// log2 units (scores times scale * log2(e)) so every exponential is one v_exp_f32.
 
 #include "device_util.h"
 #include "kernels.h"
@@ -35,8 +39,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = 16;           // tokens per wave work unit
-constexpr float kEmptyMax = -1e30f;  // running max before any visible key (finite)
+constexpr int kChunk = 16;                   // tokens per chunk (never straddles a page)
+constexpr int kTokPerWave = kChunk / kWaves; // consecutive tokens of a chunk per wave
+constexpr float kEmptyMax = -1e30f;          // running max before any visible key (finite)
+
+template <int D>
+struct DecodeGeometry {
+  static constexpr int kLanesPerHead = D / 8;          // 16 B (8 bf16) per lane
+  static constexpr int kHeads = 64 / kLanesPerHead;    // heads per wave load
+};
 
 template <int D>
 __global__ void __launch_bounds__(kThreads)
@@ -47,17 +58,13 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       float* __restrict__ ws_ml, float scale_log2, int num_q_heads,
                       int num_kv_heads, int log2_ps, int max_pages, int split_tokens,
                       int max_splits) {
-  constexpr int kLanesPerRow = D / 8;        // 16 B (8 bf16) per lane
-  constexpr int kRowsPerLoad = 64 / kLanesPerRow;
-  constexpr int kLoads = kChunk / kRowsPerLoad;
-  constexpr int kGroups = kWaves * kRowsPerLoad;
+  using G = DecodeGeometry<D>;
+  __shared__ float sm_o[kWaves][G::kHeads][D];
+  __shared__ float sm_m[kWaves][G::kHeads];
+  __shared__ float sm_l[kWaves][G::kHeads];
 
-  __shared__ float sm_o[kGroups][D];
-  __shared__ float sm_m[kGroups];
-  __shared__ float sm_l[kGroups];
-
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
+  const int hg = blockIdx.x;
+  const int split = blockIdx.y;
   const int b = blockIdx.z;
   const int seq_len = seq_lens[b];
   const int t_begin = split * split_tokens;
@@ -65,18 +72,21 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int t_end = min(seq_len, t_begin + split_tokens);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int row = lane / kLanesPerRow;
-  const int col = lane % kLanesPerRow;
-  const int hk = h / (num_q_heads / num_kv_heads);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane / G::kLanesPerHead;
+  const int col = lane % G::kLanesPerHead;
+  const int h = hg * G::kHeads + row;          // query head of this row group
+  const bool active = h < num_q_heads;
+  const int hk = (active ? h : 0) / (num_q_heads / num_kv_heads);
   const int ps_mask = (1 << log2_ps) - 1;
   const size_t token_stride = (size_t)num_kv_heads * D;  // elements between tokens
 
   // query slice of this lane, pre-multiplied by scale * log2(e)
   float qf[8];
   {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(
-        q + ((size_t)b * num_q_heads + h) * D + col * 8);
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (active)
+      w = *reinterpret_cast<const u32x4*>(q + ((size_t)b * num_q_heads + h) * D + col * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qf[2 * i] = bf16_lo(w[i]) * scale_log2;
@@ -84,35 +94,28 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
   }
 
-  // chunks of this split handled by this wave: wave, wave + 4, ...
+  // physical page of each chunk of the split, one per lane (split_tokens <= 64 * 16)
   const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
-  const int my_chunks = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
-
-  // physical page of each of this wave's chunks, one per lane
-  int my_page = 0;
-  if (lane < my_chunks) {
-    const int t0 = t_begin + (wave + lane * kWaves) * kChunk;
-    my_page = block_table[(size_t)b * max_pages + (t0 >> log2_ps)];
-  }
+  int chunk_page = 0;
+  if (lane < n_chunks)
+    chunk_page = block_table[(size_t)b * max_pages + ((t_begin + lane * kChunk) >> log2_ps)];
 
   float m = kEmptyMax, l = 0.f;
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
 
-  u32x4 kbuf[kLoads], vbuf[kLoads];
-
+  // loads of this wave's tokens of chunk c
   auto issue = [&](int c, u32x4* kd, u32x4* vd) {
-    const int t0 = t_begin + (wave + c * kWaves) * kChunk;
-    const int phys = __builtin_amdgcn_readlane(my_page, c);
-    const size_t base =
-        (((size_t)phys << log2_ps) + (t0 & ps_mask)) * token_stride + (size_t)hk * D + col * 8;
+    const int t0 = t_begin + c * kChunk + wave * kTokPerWave;
+    const int phys = __builtin_amdgcn_readlane(chunk_page, c);
+    const size_t base = (((size_t)phys << log2_ps) + (t0 & ps_mask)) * token_stride +
+                        (size_t)hk * D + col * 8;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int r = i * kRowsPerLoad + row;
-      if (t0 + r < t_end) {
-        kd[i] = *reinterpret_cast<const u32x4*>(k_pool + base + r * token_stride);
-        vd[i] = *reinterpret_cast<const u32x4*>(v_pool + base + r * token_stride);
+    for (int i = 0; i < kTokPerWave; ++i) {
+      if (active && t0 + i < t_end) {
+        kd[i] = *reinterpret_cast<const u32x4*>(k_pool + base + i * token_stride);
+        vd[i] = *reinterpret_cast<const u32x4*>(v_pool + base + i * token_stride);
       } else {
         kd[i] = u32x4{0u, 0u, 0u, 0u};
         vd[i] = u32x4{0u, 0u, 0u, 0u};
@@ -120,39 +123,29 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
   };
 
-  if (my_chunks > 0) issue(0, kbuf, vbuf);
-
-  for (int c = 0; c < my_chunks; ++c) {
-    u32x4 kc[kLoads], vc[kLoads];
+  auto consume = [&](int c, const u32x4* kc, const u32x4* vc) {
+    const int t0 = t_begin + c * kChunk + wave * kTokPerWave;
+    float s[kTokPerWave];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      kc[i] = kbuf[i];
-      vc[i] = vbuf[i];
-    }
-    if (c + 1 < my_chunks) issue(c + 1, kbuf, vbuf);
-
-    const int t0 = t_begin + (wave + c * kWaves) * kChunk;
-    float s[kLoads];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < kTokPerWave; ++i) {
       float acc = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         acc = fmaf(qf[2 * w], bf16_lo(kc[i][w]), acc);
         acc = fmaf(qf[2 * w + 1], bf16_hi(kc[i][w]), acc);
       }
-      acc = group_sum<kLanesPerRow>(acc);
-      s[i] = (t0 + i * kRowsPerLoad + row < t_end) ? acc : -INFINITY;
+      acc = group_sum<G::kLanesPerHead>(acc);
+      s[i] = (t0 + i < t_end) ? acc : -INFINITY;
     }
     float mx = s[0];
 #pragma unroll
-    for (int i = 1; i < kLoads; ++i) mx = fmaxf(mx, s[i]);
+    for (int i = 1; i < kTokPerWave; ++i) mx = fmaxf(mx, s[i]);
     const float m_new = fmaxf(m, mx);
     const float alpha = fast_exp2(m - m_new);
     float psum = 0.f;
-    float p[kLoads];
+    float p[kTokPerWave];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < kTokPerWave; ++i) {
       p[i] = fast_exp2(s[i] - m_new);
       psum += p[i];
     }
@@ -162,7 +155,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       float lo = o[2 * w] * alpha;
       float hi = o[2 * w + 1] * alpha;
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
+      for (int i = 0; i < kTokPerWave; ++i) {
         lo = fmaf(p[i], bf16_lo(vc[i][w]), lo);
         hi = fmaf(p[i], bf16_hi(vc[i][w]), hi);
       }
@@ -170,29 +163,48 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       o[2 * w + 1] = hi;
     }
     m = m_new;
+  };
+
+  // three register buffers: chunk c is consumed while c+1 and c+2 are in flight
+  u32x4 ka[kTokPerWave], va[kTokPerWave], kb[kTokPerWave], vb[kTokPerWave];
+  u32x4 kc[kTokPerWave], vc[kTokPerWave];
+  issue(0, ka, va);
+  if (n_chunks > 1) issue(1, kb, vb);
+  for (int c = 0; c < n_chunks; c += 3) {
+    if (c + 2 < n_chunks) issue(c + 2, kc, vc);
+    consume(c, ka, va);
+    if (c + 1 >= n_chunks) break;
+    if (c + 3 < n_chunks) issue(c + 3, ka, va);
+    consume(c + 1, kb, vb);
+    if (c + 2 >= n_chunks) break;
+    if (c + 4 < n_chunks) issue(c + 4, kb, vb);
+    consume(c + 2, kc, vc);
   }
 
-  // merge the workgroup's row groups
-  const int g = wave * kRowsPerLoad + row;
+  // merge the 4 waves' states per head and write the split's partial
 #pragma unroll
-  for (int i = 0; i < 8; ++i) sm_o[g][col * 8 + i] = o[i];
+  for (int i = 0; i < 8; ++i) sm_o[wave][row][col * 8 + i] = o[i];
   if (col == 0) {
-    sm_m[g] = m;
-    sm_l[g] = l;
+    sm_m[wave][row] = m;
+    sm_l[wave][row] = l;
   }
   __syncthreads();
-  const size_t slot = ((size_t)b * num_q_heads + h) * max_splits + split;
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    float big = sm_m[0];
+  for (int idx = threadIdx.x; idx < G::kHeads * D; idx += kThreads) {
+    const int r = idx / D;
+    const int d = idx % D;
+    const int hh = hg * G::kHeads + r;
+    if (hh >= num_q_heads) continue;
+    float big = sm_m[0][r];
 #pragma unroll
-    for (int j = 1; j < kGroups; ++j) big = fmaxf(big, sm_m[j]);
+    for (int w = 1; w < kWaves; ++w) big = fmaxf(big, sm_m[w][r]);
     float acc = 0.f, lsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j) {
-      const float w = fast_exp2(sm_m[j] - big);
-      acc = fmaf(w, sm_o[j][d], acc);
-      lsum = fmaf(w, sm_l[j], lsum);
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = fast_exp2(sm_m[w][r] - big);
+      acc = fmaf(wt, sm_o[w][r][d], acc);
+      lsum = fmaf(wt, sm_l[w][r], lsum);
     }
+    const size_t slot = ((size_t)b * num_q_heads + hh) * max_splits + split;
     ws_o[slot * D + d] = acc;
     if (d == 0) {
       ws_ml[slot * 2] = big;
@@ -224,22 +236,21 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
   out[((size_t)b * num_q_heads + h) * D + d] = to_bf16_bits(r);
 }
 
+template <int D>
+void launch_partial(const DecodeArgs& a, hipStream_t stream) {
+  using G = DecodeGeometry<D>;
+  const dim3 grid((a.num_q_heads + G::kHeads - 1) / G::kHeads, a.max_splits, a.batch);
+  hipLaunchKernelGGL(decode_partial_kernel<D>, grid, dim3(kThreads), 0, stream, a.q, a.k_pool,
+                     a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
+                     score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
+                     a.log2_page_size, a.max_pages_per_seq, a.split_tokens, a.max_splits);
+}
+
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.max_splits, a.num_q_heads, a.batch);
-  const float c = score_scale_log2(a.scale);
-  if (a.head_dim == 128) {
-    hipLaunchKernelGGL(decode_partial_kernel<128>, grid, dim3(kThreads), 0, stream, a.q,
-                       a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml, c,
-                       a.num_q_heads, a.num_kv_heads, a.log2_page_size, a.max_pages_per_seq,
-                       a.split_tokens, a.max_splits);
-  } else {
-    hipLaunchKernelGGL(decode_partial_kernel<64>, grid, dim3(kThreads), 0, stream, a.q,
-                       a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml, c,
-                       a.num_q_heads, a.num_kv_heads, a.log2_page_size, a.max_pages_per_seq,
-                       a.split_tokens, a.max_splits);
-  }
+  if (a.head_dim == 128) launch_partial<128>(a, stream);
+  else launch_partial<64>(a, stream);
   return hipGetLastError();
 }
 

@@ -51,8 +51,9 @@ struct DecodeArgs {
 constexpr int kPrefillBlockM = 128;
 constexpr int kPrefillBlockN = 64;
 
-// Keys per decode split when pages are at most this long.
-constexpr int kDecodeSplitTokens = 512;
+// Keys per decode split when pages are at most this long (a split's chunk pages are
+// fetched one per lane, so a split holds at most 64 chunks of 16 tokens).
+constexpr int kDecodeSplitTokens = 256;
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);

@@ -81,14 +81,14 @@ def test_prefill_empty_batch_is_ok_without_device(lib):
 
 def test_decode_workspace_size_formula(lib):
     layout = B.make_layout(17000, 16, 32, 128, 512)
-    # 512 pages x 16 tokens, 512-token splits -> 16 splits per sequence
-    assert lib.pa_decode_split_tokens(ctypes.byref(layout)) == 512
-    o = 64 * 32 * 16 * 128 * 4
-    ml = 64 * 32 * 16 * 2 * 4
+    # 512 pages x 16 tokens, 256-token splits -> 32 splits per sequence
+    assert lib.pa_decode_split_tokens(ctypes.byref(layout)) == 256
+    o = 64 * 32 * 32 * 128 * 4
+    ml = 64 * 32 * 32 * 2 * 4
     r = lambda n: (n + 255) // 256 * 256
     assert lib.pa_decode_workspace_bytes(64, 32, ctypes.byref(layout)) == r(o) + r(ml)
     big = B.make_layout(128, 256, 8, 128, 128)
-    assert lib.pa_decode_split_tokens(ctypes.byref(big)) == 512
+    assert lib.pa_decode_split_tokens(ctypes.byref(big)) == 256
     bad = B.make_layout(128, 24, 8, 128, 128)
     assert lib.pa_decode_workspace_bytes(1, 8, ctypes.byref(bad)) == 0
 

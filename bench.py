@@ -82,7 +82,8 @@ def source_digest(kind: str) -> str:
 def recorded_traffic(kind: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None if absent or
     if the kernel sources changed since the counters were taken."""
-    path = os.path.join(PROFILES, f"{kind}_{workload}_traffic.txt")
+    kernel = "decode_partial_kernel" if kind == "decode" else "prefill_kernel"
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -257,6 +258,73 @@ def cpu_baseline_prefill(wl, call, budget_s=15.0):
     }
 
 
+# ------------------------------------------------------------------ rocprofv3 summaries
+
+KERNEL_TAGS = {"decode": "decode_partial_kernel", "prefill": "prefill_kernel<128, true>",
+               "prefill_noncausal": "prefill_kernel<128, false>"}
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(trace_dir, out_path, command):
+    """Writes the kernel-trace statistics of a rocprofv3 --kernel-trace --stats run."""
+    rows = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    lines = ["# rocprofv3 kernel statistics (durations in microseconds)",
+             f"# command: {command}",
+             f"# {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"  {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f}  {short}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_traffic(fetch_dir, write_dir, kind, workload, out_path, command):
+    """HBM bytes per launch of one kernel from FETCH_SIZE and WRITE_SIZE runs, each
+    scaled by what the same counter reads for a plain 1 GiB device copy."""
+    tag = KERNEL_TAGS[kind]
+    gib_kib = float(1 << 20)
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv"))
+                if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 131072
+                  and float(r["Counter_Value"]) > gib_kib / 4]
+        kern = [float(r["Counter_Value"]) for r in rows if tag in r["Kernel_Name"]]
+        if not copies or not kern:
+            raise SystemExit(f"{counter}: no calibration copy or no {tag} dispatch in {d}")
+        factor = gib_kib / (sum(copies) / len(copies))
+        res[counter] = (sum(kern) / len(kern), factor, len(kern))
+    fetch_kib, f_fac, n = res["FETCH_SIZE"]
+    write_kib, w_fac, _ = res["WRITE_SIZE"]
+    hbm = (fetch_kib * f_fac + write_kib * w_fac) * 1024
+    src = "decode" if kind == "decode" else "prefill"
+    lines = [f"# HBM traffic per launch of {tag} on workload {workload}",
+             f"# command (run twice, once per counter): {command}",
+             "# each counter is scaled by (1 GiB / its reading for a plain 1 GiB device copy);",
+             "# bench.py reports this figure only while source_sha256 matches the kernel sources",
+             f"kernel={tag}",
+             f"workload={workload}",
+             f"dispatches={n}",
+             f"fetch_kib_raw={fetch_kib:.1f}",
+             f"fetch_copy_factor={f_fac:.4f}",
+             f"write_kib_raw={write_kib:.1f}",
+             f"write_copy_factor={w_fac:.4f}",
+             f"hbm_bytes_per_launch={hbm:.0f}",
+             f"source_sha256={source_digest(src)}"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -270,7 +338,20 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                    help="write a kernel-statistics summary of a rocprofv3 run and exit")
+    ap.add_argument("--summarize-traffic", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "KIND", "WORKLOAD", "OUT"),
+                    help="write the calibrated HBM traffic of one kernel and exit")
+    ap.add_argument("--profile-command", default="",
+                    help="the command recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.profile_command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.profile_command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -331,6 +412,14 @@ def main():
                          "kernel_ms_avg": round(split_avg, 4),
                          "combine_ms_avg": round(sum(comb_ms) / len(comb_ms), 4)},
         })
+        if len(wl.calls) > 1:  # mixed batch: the prefill chunks on the same pools
+            chunks = wl.calls[1]
+            cs = prefill_summary(wl, chunks, args.steps, args.warmup)
+            t_roof = nbytes / (HBM_PEAK_GBS * 1e9) + cs["flops_per_launch"] / (
+                MFMA_BF16_PEAK_TFLOPS * 1e12)
+            t_meas = (split_avg + sum(comb_ms) / len(comb_ms) + cs["kernel_ms_avg"]) * 1e-3
+            result["chunks"] = cs
+            result["combined_roofline_fraction"] = round(t_roof / t_meas, 4)
         if not args.no_cpu_baseline:
             log("cpu baseline (oracle) on a bounded sample")
             result["cpu_baseline"] = cpu_baseline_decode(wl, call)

@@ -26,7 +26,8 @@
 //     are merged through LDS and the split's (m, l, unnormalised O) goes to the
 //     workspace.
 //   pass 2 (decode_combine_kernel): per (sequence, head), merges the splits'
-//     partials with the same rescaling algebra and writes bf16 O.
+//     partials with the same rescaling algebra (4 waves share the splits) and
+//     writes bf16 O.
 //
 // Query head h reads K/V head h / (num_q_heads / num_kv_heads).  m is kept in
 // log2 units (scores times scale * log2(e)) so every exponential is one v_exp_f32.
@@ -213,27 +214,64 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
 }
 
+// One workgroup per (sequence, head): the global max of the splits' m first, then
+// the 4 waves take every 4th split (lanes cover d), then an LDS sum of the waves.
+constexpr int kCombineThreads = 256;
+
 template <int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(kCombineThreads)
 decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restrict__ ws_o,
                       const float* __restrict__ ws_ml, uint16_t* __restrict__ out,
                       int num_q_heads, int split_tokens, int max_splits) {
+  constexpr int kPerLane = D / 64;
+  __shared__ float sm_max[kWaves];
+  __shared__ float sm_l[kWaves];
+  __shared__ float sm_acc[kWaves][D];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int seq_len = seq_lens[b];
   const int n_splits = seq_len > 0 ? (seq_len + split_tokens - 1) / split_tokens : 0;
   const size_t slot0 = ((size_t)b * num_q_heads + h) * max_splits;
-  float big = kEmptyMax;
-  for (int s = 0; s < n_splits; ++s) big = fmaxf(big, ws_ml[(slot0 + s) * 2]);
-  float acc = 0.f, lsum = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float w = fast_exp2(ws_ml[(slot0 + s) * 2] - big);
-    acc = fmaf(w, ws_o[(slot0 + s) * D + d], acc);
-    lsum = fmaf(w, ws_ml[(slot0 + s) * 2 + 1], lsum);
+
+  float mx = kEmptyMax;
+  for (int s = threadIdx.x; s < n_splits; s += kCombineThreads)
+    mx = fmaxf(mx, ws_ml[(slot0 + s) * 2]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) sm_max[wave] = mx;
+  __syncthreads();
+  float big = sm_max[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) big = fmaxf(big, sm_max[w]);
+
+  float acc[kPerLane];
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) acc[e] = 0.f;
+  float lsum = 0.f;
+  for (int s = wave; s < n_splits; s += kWaves) {
+    const float m_s = ws_ml[(slot0 + s) * 2];
+    const float l_s = ws_ml[(slot0 + s) * 2 + 1];
+    const float w = fast_exp2(m_s - big);
+    const float* o_s = ws_o + (slot0 + s) * D + lane * kPerLane;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) acc[e] = fmaf(w, o_s[e], acc[e]);
+    lsum = fmaf(w, l_s, lsum);
   }
-  const float r = lsum > 0.f ? acc / lsum : 0.f;
-  out[((size_t)b * num_q_heads + h) * D + d] = to_bf16_bits(r);
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) sm_acc[wave][lane * kPerLane + e] = acc[e];
+  if (lane == 0) sm_l[wave] = lsum;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      o += sm_acc[w][threadIdx.x];
+      l += sm_l[w];
+    }
+    const float r = l > 0.f ? o / l : 0.f;
+    out[((size_t)b * num_q_heads + h) * D + threadIdx.x] = to_bf16_bits(r);
+  }
 }
 
 template <int D>
@@ -257,11 +295,13 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.batch);
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(128), 0, stream, a.seq_lens,
-                       a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens, a.max_splits);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(kCombineThreads), 0, stream,
+                       a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
+                       a.max_splits);
   } else {
-    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64), 0, stream, a.seq_lens,
-                       a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens, a.max_splits);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(kCombineThreads), 0, stream,
+                       a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
+                       a.max_splits);
   }
   return hipGetLastError();
 }

@@ -261,23 +261,30 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
 
-    // P = exp2(s * c - m_ref), bf16 for the MFMA, row-sum partial in fp32
+    // P = exp2(s * c - m_ref) rounded to bf16 for the MFMA; the row sum adds exactly
+    // those rounded values (two per v_dot2 against (1, 1)), so the weights applied to V
+    // sum to l.  The packed words are kept as scalars: building the dot2 operands from
+    // vector elements is miscompiled by this compiler.
     bf16x8 pb[4];
-    float lsum = 0.f;
+    float lsum0 = 0.f, lsum1 = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      u32x4 w;
+      uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x0 = fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e], scale_log2, -m_ref));
         const float x1 =
             fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e + 1], scale_log2, -m_ref));
-        lsum += x0 + x1;
         w[e] = pack_bf16x2(x0, x1);
       }
-      pb[c] = __builtin_bit_cast(bf16x8, w);
+      lsum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0]), ones, lsum0, false);
+      lsum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[1]), ones, lsum1, false);
+      lsum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2]), ones, lsum0, false);
+      lsum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[3]), ones, lsum1, false);
+      pb[c] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
     }
-    l_part += lsum;
+    l_part += lsum0 + lsum1;
 
     // O^T (d x queries) += V^T P^T
 #pragma unroll

@@ -323,8 +323,9 @@ def test_constant_values_return_the_constant():
         wl.v_pool[used] = 1.75
         out = G.run_call(wl, wl.calls[0]).float()
         torch.cuda.synchronize()
-        # within one bf16 ulp of 1.75 (ulp 2^-7 in [1, 2))
-        assert (out - 1.75).abs().max().item() <= 2 ** -7, kind
+        # the row sum adds exactly the weights applied to V (prefill: the bf16-rounded P;
+        # decode: the fp32 P), so O = c up to fp32 rounding, which bf16 rounds back to c
+        assert torch.all(out == 1.75), (kind, (out - 1.75).abs().max().item())
 
 
 def test_empty_batch_and_zero_rows_are_no_ops():

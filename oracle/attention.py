@@ -33,6 +33,11 @@ Readings where the pages leave a step open:
   * A decode query is the newest token, already appended to the cache, and
     sees all L keys of its sequence (KV-cache flowchart, "Append new K_t, V_t").
   * The scale is the fp32 value handed to the kernel, widened exactly to fp64.
+  * Sliding window ("What do FlashAttention and PagedAttention actually
+    optimize?", section "Sort techniques into the two bins": attention over only
+    the previous w tokens): with window w >= 1 a query at position p sees the w
+    keys p - w + 1 .. p (its own key included); window 0 means no window.  Only
+    meaningful together with causal attention.
 
 Inputs are raw bf16 bit patterns (uint16 arrays).  Decoding them to fp64 is
 exact.  The output stays in fp64; nothing here rounds to bf16.
@@ -101,16 +106,24 @@ def gather_sequence(pool_bits: np.ndarray, block_table_row: Sequence[int],
     return bf16_to_f64(rows)
 
 
-def visible_mask(positions: np.ndarray, seq_len: int, causal: bool) -> np.ndarray:
+def visible_mask(positions: np.ndarray, seq_len: int, causal: bool,
+                 window: int = 0) -> np.ndarray:
     """Boolean [rows, L]: key t is visible to a query at absolute position p.
 
     Non-causal: every key 0 <= t < L.  Causal: keys t <= p (bottom-right
-    alignment; see the module docstring).
+    alignment; see the module docstring).  Window w > 0 (causal only): also
+    t >= p - w + 1.
     """
     keys = np.arange(seq_len)
     if not causal:
+        if window:
+            raise ValueError("a sliding window needs causal attention")
         return np.ones((len(positions), seq_len), dtype=bool)
-    return keys[None, :] <= np.asarray(positions)[:, None]
+    pos = np.asarray(positions)[:, None]
+    mask = keys[None, :] <= pos
+    if window:
+        mask &= keys[None, :] >= pos - window + 1
+    return mask
 
 
 def scores(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
@@ -142,7 +155,7 @@ def weighted_values(p: np.ndarray, values: np.ndarray) -> np.ndarray:
 
 
 def attend(q_rows: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
-           positions: np.ndarray, causal: bool, scale: float):
+           positions: np.ndarray, causal: bool, scale: float, window: int = 0):
     """Attention of some query rows of one sequence over its gathered keys.
 
     q_rows [r, H, d] fp64, k_seq / v_seq [L, H, d] fp64, positions [r] absolute.
@@ -155,7 +168,7 @@ def attend(q_rows: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
     for h in range(heads):
         for r0 in range(0, r, ROW_BLOCK):
             r1 = min(r, r0 + ROW_BLOCK)
-            mask = visible_mask(positions[r0:r1], seq_len, causal)
+            mask = visible_mask(positions[r0:r1], seq_len, causal, window)
             s = scores(q_rows[r0:r1, h, :], k_seq[:, h, :], scale)
             p, row_lse = softmax_rows(s, mask)
             out[r0:r1, h, :] = weighted_values(p, v_seq[:, h, :])
@@ -164,7 +177,7 @@ def attend(q_rows: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
 
 
 def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_start,
-                  causal: bool, scale: float, rows: Optional[dict] = None):
+                  causal: bool, scale: float, rows: Optional[dict] = None, window: int = 0):
     """Prefill (or chunked prefill) over a paged cache.
 
     q_bits       uint16 [total_q, H, d]; rows of sequence b are q_start[b]..q_start[b+1]-1
@@ -173,6 +186,7 @@ def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_sta
     seq_lens     int [batch]: L_b, the KV length including this chunk
     scale        the fp32 scale value (widened exactly)
     rows         optional {b: array of local row indices} to evaluate only some rows
+    window       sliding-window length w (0: none); needs causal
 
     Returns (O fp64 [total_q, H, d] with NaN where not evaluated, lse [total_q, H]).
     """
@@ -197,15 +211,16 @@ def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_sta
         v_seq = gather_sequence(v_pool_bits, block_table[b], seq_len, page_size)
         positions = seq_len - q_len + local
         q_rows = bf16_to_f64(q_bits[start + local])
-        o, l = attend(q_rows, k_seq, v_seq, positions, causal, scale)
+        o, l = attend(q_rows, k_seq, v_seq, positions, causal, scale, window)
         out[start + local] = o
         lse[start + local] = l
     return out, lse
 
 
 def paged_decode(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, scale: float,
-                 seqs: Optional[Sequence[int]] = None):
-    """Decode: one query token per sequence over all L_b cached keys (itself included).
+                 seqs: Optional[Sequence[int]] = None, window: int = 0):
+    """Decode: one query token per sequence over all L_b cached keys (itself included),
+    or over the last `window` of them when window > 0.
 
     q_bits uint16 [batch, H, d].  Returns (O fp64 [batch, H, d], lse [batch, H]);
     sequences not in `seqs` are left NaN.
@@ -223,7 +238,8 @@ def paged_decode(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, scale:
         k_seq = gather_sequence(k_pool_bits, block_table[b], seq_len, page_size)
         v_seq = gather_sequence(v_pool_bits, block_table[b], seq_len, page_size)
         q_rows = bf16_to_f64(q_bits[b:b + 1])
-        o, l = attend(q_rows, k_seq, v_seq, np.array([seq_len - 1]), False, scale)
+        o, l = attend(q_rows, k_seq, v_seq, np.array([seq_len - 1]), window > 0, scale,
+                      window)
         out[b] = o[0]
         lse[b] = l[0]
     return out, lse

@@ -65,7 +65,7 @@ def random_paged_case(rng, batch, heads, d, page_size, lens, q_lens, extra_pages
     return dict(q=q, k=k, v=v, table=table, lens=np.array(lens), q_start=q_start)
 
 
-def brute_force(q, k, v, table, lens, q_start, causal, scale):
+def brute_force(q, k, v, table, lens, q_start, causal, scale, window=0):
     """Scalar Python loops with math.exp; walks each sequence's pages in table order.
 
     Written independently of oracle.attention: no numpy arithmetic, and the
@@ -96,9 +96,10 @@ def brute_force(q, k, v, table, lens, q_start, causal, scale):
         for i in range(q_len):
             row = int(q_start[b]) + i
             last = L - q_len + i if causal else L - 1
+            first = max(0, last - window + 1) if window else 0
             for h in range(heads):
                 s = []
-                for t in range(last + 1):
+                for t in range(first, last + 1):
                     acc = 0.0
                     for c in range(d):
                         acc += qf[row][h][c] * keys[t][h][c]
@@ -108,8 +109,8 @@ def brute_force(q, k, v, table, lens, q_start, causal, scale):
                 tot = sum(e)
                 for c in range(d):
                     acc = 0.0
-                    for t in range(last + 1):
-                        acc += e[t] * vals[t][h][c]
+                    for t in range(first, last + 1):
+                        acc += e[t - first] * vals[t][h][c]
                     out[row][h][c] = acc / tot
     return np.array(out)
 
@@ -355,6 +356,63 @@ def pin_decode_matches_last_row(seed=6) -> bool:
     return bool(np.max(np.abs(dec - full[last_rows])) < 1e-14)
 
 
+def pin_sliding_window(seed=7) -> bool:
+    """Window w (the previous w tokens, own key included): brute force on chunked
+    causal cases; w = 1 returns the query's own V row; w >= L changes no bit; a band
+    mask in float64 SDPA agrees; decode sees the last w keys."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(seed)
+    case = random_paged_case(rng, 2, 2, 4, 4, [13, 9], [6, 9])
+    scale = float(np.float32(0.41))
+    for w in (1, 3, 7):
+        want = brute_force(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                           case["q_start"], True, scale, window=w)
+        got, _ = A.paged_prefill(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                                 case["q_start"], True, scale, window=w)
+        if np.max(np.abs(got - want)) > 1e-13:
+            return False
+    # w = 1: only the query's own key -> its V row, exactly
+    got, _ = A.paged_prefill(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                             case["q_start"], True, scale, window=1)
+    for b, L in enumerate(case["lens"]):
+        q0, q1 = case["q_start"][b], case["q_start"][b + 1]
+        for i in range(q1 - q0):
+            t = L - (q1 - q0) + i
+            phys = case["table"][b][t // 4]
+            if not np.array_equal(got[q0 + i], A.bf16_to_f64(case["v"][phys, t % 4])):
+                return False
+    # a window covering everything is no window
+    full, _ = A.paged_prefill(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                              case["q_start"], True, scale)
+    wide, _ = A.paged_prefill(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                              case["q_start"], True, scale, window=13)
+    if not np.array_equal(full, wide):
+        return False
+    # SDPA with an explicit band mask, identity table
+    L, q_len, heads, d, ps, w = 40, 40, 2, 8, 8, 5
+    n = A.pages_needed(L, ps)
+    k = to_bf16_bits(rng.normal(size=(n, ps, heads, d)))
+    v = to_bf16_bits(rng.normal(size=(n, ps, heads, d)))
+    q = to_bf16_bits(rng.normal(size=(q_len, heads, d)))
+    got, _ = A.paged_prefill(q, k, v, np.arange(n)[None, :], [L], [0, q_len], True, scale,
+                             window=w)
+    kk = torch.from_numpy(A.bf16_to_f64(k).reshape(n * ps, heads, d)[:L]).permute(1, 0, 2)
+    vv = torch.from_numpy(A.bf16_to_f64(v).reshape(n * ps, heads, d)[:L]).permute(1, 0, 2)
+    qq = torch.from_numpy(A.bf16_to_f64(q)).permute(1, 0, 2)
+    band = torch.ones(q_len, L, dtype=torch.bool).tril(0) & ~torch.ones(q_len, L, dtype=torch.bool).tril(-w)
+    ref = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=band, scale=scale)
+    if np.max(np.abs(got - ref.permute(1, 0, 2).numpy())) > 1e-12:
+        return False
+    # decode with a window = last row of the windowed causal prefill
+    last_rows = case["q_start"][1:] - 1
+    dec, _ = A.paged_decode(case["q"][last_rows], case["k"], case["v"], case["table"],
+                            case["lens"], scale, window=3)
+    pre, _ = A.paged_prefill(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                             case["q_start"], True, scale, window=3)
+    return bool(np.max(np.abs(dec - pre[last_rows])) < 1e-14)
+
+
 ALL_PINS = [
     pin_practical_example_translation,
     pin_practical_example_gather,
@@ -366,6 +424,7 @@ ALL_PINS = [
     pin_shared_prefix,
     pin_rows_sum_to_one,
     pin_decode_matches_last_row,
+    pin_sliding_window,
 ]
 
 

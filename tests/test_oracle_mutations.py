@@ -20,14 +20,22 @@ def _offset_off_by_one(row, t, ps):
     return t // ps, (t + 1) % ps, int(row[t // ps])
 
 
-def _causal_strict(positions, L, causal):
+def _window_off_by_one(positions, L, causal, window=0):
+    mask = _ORIG["visible_mask"](positions, L, causal)
+    if window:
+        keys = np.arange(L)
+        mask &= keys[None, :] >= np.asarray(positions)[:, None] - window
+    return mask
+
+
+def _causal_strict(positions, L, causal, window=0):
     keys = np.arange(L)
     if not causal:
         return np.ones((len(positions), L), dtype=bool)
     return keys[None, :] < np.asarray(positions)[:, None]
 
 
-def _causal_top_left(positions, L, causal):
+def _causal_top_left(positions, L, causal, window=0):
     keys = np.arange(L)
     if not causal:
         return np.ones((len(positions), L), dtype=bool)
@@ -76,6 +84,7 @@ MUTANTS = [
     ("locate_token", _offset_off_by_one),
     ("visible_mask", _causal_strict),
     ("visible_mask", _causal_top_left),
+    ("visible_mask", _window_off_by_one),
     ("scores", _no_scale),
     ("scores", _scale_squared),
     ("softmax_rows", _mask_after_softmax),

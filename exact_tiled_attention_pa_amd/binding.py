@@ -28,8 +28,8 @@ PA_ERR_HIP = 5
 # Every symbol the header declares.
 EXPORTED = (
     "pa_prefill", "pa_decode_workspace_bytes", "pa_decode_split_tokens", "pa_decode",
-    "pa_decode_partial", "pa_decode_combine", "pa_status_string", "pa_last_error",
-    "pa_version",
+    "pa_decode_partial", "pa_decode_combine", "pa_prefill_window", "pa_decode_window",
+    "pa_status_string", "pa_last_error", "pa_version",
 )
 
 
@@ -79,6 +79,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_decode_partial.restype = ctypes.c_int
     lib.pa_decode_combine.argtypes = [vp, vp, i32, i32, vp, sz, lay, vp]
     lib.pa_decode_combine.restype = ctypes.c_int
+    lib.pa_prefill_window.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, f32, vp, vp, i32, i32,
+                                      i32, i32, lay, vp]
+    lib.pa_prefill_window.restype = ctypes.c_int
+    lib.pa_decode_window.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, vp, sz, lay, vp]
+    lib.pa_decode_window.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
@@ -139,9 +144,10 @@ def _check_device_tensors(**tensors):
 
 
 def pa_prefill(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_start,
-               max_q_len: int, stream=None):
+               max_q_len: int, stream=None, window: int = 0):
     """Paged (chunked) prefill: out[q_start[b]:q_start[b+1]] = attention of sequence b's
-    query rows over its L_b = seq_lens[b] paged keys.  See pa_prefill in pagedattn.h."""
+    query rows over its L_b = seq_lens[b] paged keys.  See pa_prefill in pagedattn.h;
+    window > 0 calls pa_prefill_window."""
     _check_device_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
                           seq_lens=seq_lens, out=out, q_start=q_start)
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
@@ -155,10 +161,16 @@ def pa_prefill(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_s
     _require(block_table.dim() == 2 and block_table.shape[0] >= batch, "block_table: [batch, maxp]")
     _require(q_start.numel() == batch + 1, "q_start: [batch + 1]")
     lay = layout_of(k_pool, block_table)
-    st = load_library().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-                                   _ptr(seq_lens), int(bool(causal)), float(scale), _ptr(out),
-                                   _ptr(q_start), batch, q.shape[1], int(max_q_len),
-                                   ctypes.byref(lay), _stream(stream))
+    if window:
+        st = load_library().pa_prefill_window(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+            int(bool(causal)), float(scale), _ptr(out), _ptr(q_start), batch, q.shape[1],
+            int(max_q_len), int(window), ctypes.byref(lay), _stream(stream))
+    else:
+        st = load_library().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                       _ptr(seq_lens), int(bool(causal)), float(scale),
+                                       _ptr(out), _ptr(q_start), batch, q.shape[1],
+                                       int(max_q_len), ctypes.byref(lay), _stream(stream))
     _check(st)
     return out
 
@@ -197,14 +209,23 @@ def _decode_checks(q, k_pool, v_pool, block_table, seq_lens, workspace, out=None
              "seq_lens: [batch]; block_table: [batch, maxp]")
 
 
-def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace, stream=None):
-    """One query token per sequence over all its L_b cached tokens (split-KV + combine)."""
+def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace, stream=None,
+              window: int = 0):
+    """One query token per sequence over all its L_b cached tokens (split-KV + combine);
+    window > 0 calls pa_decode_window (only the last `window` tokens)."""
     _decode_checks(q, k_pool, v_pool, block_table, seq_lens, workspace, out)
     lay = layout_of(k_pool, block_table)
-    st = load_library().pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-                                  _ptr(seq_lens), float(scale), _ptr(out), q.shape[0], q.shape[1],
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  ctypes.byref(lay), _stream(stream))
+    nbytes = workspace.numel() * workspace.element_size()
+    if window:
+        st = load_library().pa_decode_window(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+            float(scale), _ptr(out), q.shape[0], q.shape[1], int(window), _ptr(workspace),
+            nbytes, ctypes.byref(lay), _stream(stream))
+    else:
+        st = load_library().pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                      _ptr(seq_lens), float(scale), _ptr(out), q.shape[0],
+                                      q.shape[1], _ptr(workspace), nbytes, ctypes.byref(lay),
+                                      _stream(stream))
     _check(st)
     return out
 

@@ -115,7 +115,8 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
 pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
                            const int32_t* block_table, const int32_t* seq_lens, float scale,
                            pa_bf16* out, int32_t batch, int32_t num_q_heads,
-                           const void* workspace, const pa_kv_layout* layout) {
+                           const void* workspace, const pa_kv_layout* layout,
+                           int32_t window = 0) {
   pa::DecodeArgs a;
   a.q = q;
   a.k_pool = k_pool;
@@ -135,6 +136,7 @@ pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf1
   a.max_pages_per_seq = layout->max_pages_per_seq;
   a.split_tokens = split_tokens_of(layout);
   a.max_splits = max_splits_of(layout);
+  a.window = window;
   return a;
 }
 
@@ -148,10 +150,15 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
-               const int32_t* block_table, const int32_t* seq_lens, int causal, float scale,
-               pa_bf16* out, const int32_t* q_start, int32_t batch, int32_t num_q_heads,
-               int32_t max_q_len, const pa_kv_layout* layout, hipStream_t stream) {
+int pa_prefill_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, int causal,
+                      float scale, pa_bf16* out, const int32_t* q_start, int32_t batch,
+                      int32_t num_q_heads, int32_t max_q_len, int32_t window,
+                      const pa_kv_layout* layout, hipStream_t stream) {
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window=%d must be >= 0", window);
+  if (window > 0 && !causal)
+    return fail(PA_ERR_INVALID_ARG, "a sliding window (window=%d) needs causal attention",
+                window);
   int st = check_layout(layout, num_q_heads);
   if (st) return st;
   if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch=%d must be >= 0", batch);
@@ -188,7 +195,16 @@ int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
   a.log2_page_size = log2_exact(layout->page_size);
   a.max_pages_per_seq = layout->max_pages_per_seq;
   a.max_q_len = max_q_len;
+  a.window = window;
   return hip_status(pa::launch_prefill(a, stream), "prefill launch");
+}
+
+int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+               const int32_t* block_table, const int32_t* seq_lens, int causal, float scale,
+               pa_bf16* out, const int32_t* q_start, int32_t batch, int32_t num_q_heads,
+               int32_t max_q_len, const pa_kv_layout* layout, hipStream_t stream) {
+  return pa_prefill_window(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out,
+                           q_start, batch, num_q_heads, max_q_len, 0, layout, stream);
 }
 
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
@@ -229,20 +245,30 @@ int pa_decode_combine(const int32_t* seq_lens, pa_bf16* out, int32_t batch,
   return hip_status(pa::launch_decode_combine(a, stream), "decode combine launch");
 }
 
-int pa_decode(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
-              const int32_t* block_table, const int32_t* seq_lens, float scale, pa_bf16* out,
-              int32_t batch, int32_t num_q_heads, void* workspace, size_t workspace_bytes,
-              const pa_kv_layout* layout, hipStream_t stream) {
+int pa_decode_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, float scale,
+                     pa_bf16* out, int32_t batch, int32_t num_q_heads, int32_t window,
+                     void* workspace, size_t workspace_bytes, const pa_kv_layout* layout,
+                     hipStream_t stream) {
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window=%d must be >= 0", window);
   int st = check_decode_common(q, k_pool, v_pool, block_table, seq_lens, scale, batch,
                                num_q_heads, workspace, workspace_bytes, layout, true);
   if (st) return st;
   if (!out) return fail(PA_ERR_NULL, "out must be non-NULL");
   if (batch == 0) return ok();
   const pa::DecodeArgs a = decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, out,
-                                       batch, num_q_heads, workspace, layout);
+                                       batch, num_q_heads, workspace, layout, window);
   st = hip_status(pa::launch_decode_partial(a, stream), "decode partial launch");
   if (st) return st;
   return hip_status(pa::launch_decode_combine(a, stream), "decode combine launch");
+}
+
+int pa_decode(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+              const int32_t* block_table, const int32_t* seq_lens, float scale, pa_bf16* out,
+              int32_t batch, int32_t num_q_heads, void* workspace, size_t workspace_bytes,
+              const pa_kv_layout* layout, hipStream_t stream) {
+  return pa_decode_window(q, k_pool, v_pool, block_table, seq_lens, scale, out, batch,
+                          num_q_heads, 0, workspace, workspace_bytes, layout, stream);
 }
 
 const char* pa_status_string(int status) {

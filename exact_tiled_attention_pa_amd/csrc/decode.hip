@@ -58,7 +58,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       const int32_t* __restrict__ seq_lens, float* __restrict__ ws_o,
                       float* __restrict__ ws_ml, float scale_log2, int num_q_heads,
                       int num_kv_heads, int log2_ps, int max_pages, int split_tokens,
-                      int max_splits) {
+                      int max_splits, int window) {
   using G = DecodeGeometry<D>;
   __shared__ float sm_o[kWaves][G::kHeads][D];
   __shared__ float sm_m[kWaves][G::kHeads];
@@ -71,6 +71,10 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int t_begin = split * split_tokens;
   if (t_begin >= seq_len) return;  // the combine pass never reads this split
   const int t_end = min(seq_len, t_begin + split_tokens);
+  // sliding window: only the last `window` keys count; earlier splits are skipped by
+  // both passes
+  const int t_lo = window > 0 ? max(0, seq_len - window) : 0;
+  if (t_end <= t_lo) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -114,7 +118,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                         (size_t)hk * D + col * 8;
 #pragma unroll
     for (int i = 0; i < kTokPerWave; ++i) {
-      if (active && t0 + i < t_end) {
+      if (active && t0 + i < t_end && t0 + i >= t_lo) {
         kd[i] = *reinterpret_cast<const u32x4*>(k_pool + base + i * token_stride);
         vd[i] = *reinterpret_cast<const u32x4*>(v_pool + base + i * token_stride);
       } else {
@@ -136,7 +140,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         acc = fmaf(qf[2 * w + 1], bf16_hi(kc[i][w]), acc);
       }
       acc = group_sum<G::kLanesPerHead>(acc);
-      s[i] = (t0 + i < t_end) ? acc : -INFINITY;
+      s[i] = (t0 + i < t_end && t0 + i >= t_lo) ? acc : -INFINITY;
     }
     float mx = s[0];
 #pragma unroll
@@ -222,7 +226,7 @@ template <int D>
 __global__ void __launch_bounds__(kCombineThreads)
 decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restrict__ ws_o,
                       const float* __restrict__ ws_ml, uint16_t* __restrict__ out,
-                      int num_q_heads, int split_tokens, int max_splits) {
+                      int num_q_heads, int split_tokens, int max_splits, int window) {
   constexpr int kPerLane = D / 64;
   __shared__ float sm_max[kWaves];
   __shared__ float sm_l[kWaves];
@@ -233,10 +237,11 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int seq_len = seq_lens[b];
   const int n_splits = seq_len > 0 ? (seq_len + split_tokens - 1) / split_tokens : 0;
+  const int s_first = window > 0 ? max(0, seq_len - window) / split_tokens : 0;
   const size_t slot0 = ((size_t)b * num_q_heads + h) * max_splits;
 
   float mx = kEmptyMax;
-  for (int s = threadIdx.x; s < n_splits; s += kCombineThreads)
+  for (int s = s_first + threadIdx.x; s < n_splits; s += kCombineThreads)
     mx = fmaxf(mx, ws_ml[(slot0 + s) * 2]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) sm_max[wave] = mx;
@@ -249,7 +254,7 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e) acc[e] = 0.f;
   float lsum = 0.f;
-  for (int s = wave; s < n_splits; s += kWaves) {
+  for (int s = s_first + wave; s < n_splits; s += kWaves) {
     const float m_s = ws_ml[(slot0 + s) * 2];
     const float l_s = ws_ml[(slot0 + s) * 2 + 1];
     const float w = fast_exp2(m_s - big);
@@ -281,7 +286,8 @@ void launch_partial(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(decode_partial_kernel<D>, grid, dim3(kThreads), 0, stream, a.q, a.k_pool,
                      a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
                      score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
-                     a.log2_page_size, a.max_pages_per_seq, a.split_tokens, a.max_splits);
+                     a.log2_page_size, a.max_pages_per_seq, a.split_tokens, a.max_splits,
+                     a.window);
 }
 
 }  // namespace
@@ -297,11 +303,11 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(kCombineThreads), 0, stream,
                        a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
-                       a.max_splits);
+                       a.max_splits, a.window);
   } else {
     hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(kCombineThreads), 0, stream,
                        a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
-                       a.max_splits);
+                       a.max_splits, a.window);
   }
   return hipGetLastError();
 }

@@ -25,6 +25,7 @@ struct PrefillArgs {
   int log2_page_size;
   int max_pages_per_seq;
   int max_q_len;
+  int window;  // sliding-window length (0: none); causal only
 };
 
 struct DecodeArgs {
@@ -45,6 +46,7 @@ struct DecodeArgs {
   int max_pages_per_seq;
   int split_tokens;
   int max_splits;
+  int window;  // sliding-window length (0: none)
 };
 
 // Rows of queries per prefill workgroup (4 waves x 32 rows) and keys per tile.

@@ -37,7 +37,10 @@
 //     kernel as the B operand; each lane ends up holding 32 scores of one query
 //     row (its query is lane % 32), so row statistics are per lane plus one
 //     exchange between lanes l and l ^ 32;
-//   - masking only on tiles that cross the causal diagonal or the sequence end;
+//   - masking only on tiles that cross the causal diagonal, the sequence end or the
+//     lower edge of a sliding window (keys p - w + 1 .. p for a row at position p;
+//     "What do FlashAttention and PagedAttention actually optimize?", "Sort
+//     techniques into the two bins"); tiles wholly below a window are skipped;
 //   - online softmax in fp32 with exp2 (scale * log2(e) folded into one FMA).  The
 //     reference max is raised only when a row's max grows by more than 8 (log2
 //     units); the output and row sum always share the same reference, so the
@@ -48,6 +51,8 @@
 //     key order of the S^T accumulator registers.
 // Epilogue: O / l, rounded to bf16 (RNE), staged through LDS and written with
 // 16-byte coalesced stores.
+
+#include <climits>
 
 #include "device_util.h"
 #include "kernels.h"
@@ -99,7 +104,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
                const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
                const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_start,
                uint16_t* __restrict__ out, float scale_log2, int num_q_heads,
-               int num_kv_heads, int log2_ps, int max_pages) {
+               int num_kv_heads, int log2_ps, int max_pages, int window) {
   using G = Geometry<D>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[G::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char k_lds1[G::kTileBytes];
@@ -126,7 +131,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
   const int row_bytes_g = num_kv_heads * D * 2;  // token stride in the pools, bytes
   const int32_t* const bt = block_table + (size_t)b * max_pages;
 
-  // key range of this workgroup and the first tile that needs a mask
+  // key range of this workgroup and the tiles that need a mask
   int kend = seq_len;
   int full_tiles = seq_len / BN;
   if (CAUSAL) {
@@ -134,6 +139,14 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     full_tiles = (shift + q0 + 1) / BN;
   }
   const int n_tiles = (kend + BN - 1) / BN;
+  // sliding window (causal only): row at position p sees keys >= p - window + 1.  The
+  // first row's bound gives the first tile; tiles below the last row's bound need masks
+  int first_tile = 0;
+  int window_masked_tiles = 0;
+  if (CAUSAL && window > 0) {
+    first_tile = max(0, shift + q0 - window + 1) / BN;
+    window_masked_tiles = (max(0, shift + q0 + BM - window) + BN - 1) / BN;
+  }
   const int last_page = seq_len > 0 ? (seq_len - 1) >> log2_ps : 0;
 
   // ---- Q fragment (B operand of S^T = K Q^T): row q0 + 32w + lane%32, 8 bf16 per k-step
@@ -205,6 +218,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
   // ---- per-lane softmax state for query row q0 + 32w + lane%32
   const int my_pos = shift + q0 + wave * 32 + l32;  // absolute position of this row
   const int wave_last_pos = shift + q0 + wave * 32 + 31;
+  const int my_lo = (CAUSAL && window > 0) ? my_pos - window + 1 : INT_MIN;  // lowest key seen
+  const int wave_lo = (CAUSAL && window > 0) ? shift + q0 + wave * 32 - window + 1 : INT_MIN;
   float m_ref = -INFINITY;  // reference max (log2 units) of O and l
   float l_part = 0.f;       // this lane's share of the row sum (its 32 keys per tile)
   f32x16 oacc[G::kDB];
@@ -230,14 +245,14 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     }
 
     // mask: register r of block kb holds key kt0 + 32kb + 8(r/4) + 4*half + r%4
-    if (j >= full_tiles) {
+    if (j >= full_tiles || j < window_masked_tiles) {
       const int lim = CAUSAL ? min(my_pos, seq_len - 1) : seq_len - 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          sacc[kb][r] = key <= lim ? sacc[kb][r] : -INFINITY;
+          sacc[kb][r] = (key <= lim && key >= my_lo) ? sacc[kb][r] : -INFINITY;
         }
     }
 
@@ -251,15 +266,20 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
 
     const bool raise = mx > m_ref + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? mx : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);
-      m_ref = m_new;
+      // lanes that do not raise keep their reference and scale by exactly 1 (their
+      // reference may still be -inf when a window has not started for their row)
+      const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;
+      m_ref = raise ? mx : m_ref;
       l_part *= alpha;
 #pragma unroll
       for (int i = 0; i < G::kDB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
+
+    // a row whose window has not started yet has seen only masked keys: its weights
+    // are exp2(-inf) = 0 whatever the reference, so use 0 instead of -inf - -inf
+    const float m_sub = m_ref == -INFINITY ? 0.f : m_ref;
 
     // P = exp2(s * c - m_ref) rounded to bf16 for the MFMA; the row sum adds exactly
     // those rounded values (two per v_dot2 against (1, 1)), so the weights applied to V
@@ -273,9 +293,9 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e], scale_log2, -m_ref));
+        const float x0 = fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e], scale_log2, -m_sub));
         const float x1 =
-            fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e + 1], scale_log2, -m_ref));
+            fast_exp2(fmaf(sacc[c >> 1][(c & 1) * 8 + 2 * e + 1], scale_log2, -m_sub));
         w[e] = pack_bf16x2(x0, x1);
       }
       lsum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0]), ones, lsum0, false);
@@ -309,12 +329,13 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j landed
     __syncthreads();                     // everyone's loads landed; tile j-1 fully consumed
     if (j + 1 < n_tiles) issue_tile(j + 1, k_nxt, v_nxt);
-    if (CAUSAL && j * BN > wave_last_pos) return;  // whole tile in this wave's future
+    if (CAUSAL && j * BN > wave_last_pos) return;        // whole tile in this wave's future
+    if (CAUSAL && j * BN + BN - 1 < wave_lo) return;     // whole tile before its window
     compute_tile(j, k_cur, v_cur);
   };
 
-  if (n_tiles > 0) issue_tile(0, k_lds0, v_lds0);
-  for (int j = 0; j < n_tiles; j += 2) {
+  if (first_tile < n_tiles) issue_tile(first_tile, k_lds0, v_lds0);
+  for (int j = first_tile; j < n_tiles; j += 2) {
     step(j, k_lds0, v_lds0, k_lds1, v_lds1);
     if (j + 1 < n_tiles) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
@@ -358,7 +379,7 @@ void launch(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a.q,
                      a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.q_start, a.out,
                      score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
-                     a.log2_page_size, a.max_pages_per_seq);
+                     a.log2_page_size, a.max_pages_per_seq, a.window);
 }
 
 }  // namespace

@@ -160,6 +160,27 @@ int pa_decode_combine(const int32_t* seq_lens, pa_bf16* out, int32_t batch,
                       int32_t num_q_heads, const void* workspace, size_t workspace_bytes,
                       const pa_kv_layout* layout, hipStream_t stream);
 
+/*
+ * Sliding-window variants ("What do FlashAttention and PagedAttention actually
+ * optimize?", section "Sort techniques into the two bins": attention over only the
+ * previous w tokens).  window = w >= 1: a query at absolute position p sees only
+ * keys p - w + 1 .. p (its own key included); window = 0: no window, identical to
+ * pa_prefill / pa_decode.  Key tiles (prefill) and splits (decode) wholly outside
+ * the window are skipped, so the work is O(rows * w).  pa_prefill_window needs
+ * causal != 0 (PA_ERR_INVALID_ARG otherwise); decode's query sits at L_b - 1.
+ * Other arguments, layouts and errors as for pa_prefill / pa_decode.
+ */
+int pa_prefill_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, int causal,
+                      float scale, pa_bf16* out, const int32_t* q_start, int32_t batch,
+                      int32_t num_q_heads, int32_t max_q_len, int32_t window,
+                      const pa_kv_layout* layout, hipStream_t stream);
+int pa_decode_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, float scale,
+                     pa_bf16* out, int32_t batch, int32_t num_q_heads, int32_t window,
+                     void* workspace, size_t workspace_bytes, const pa_kv_layout* layout,
+                     hipStream_t stream);
+
 /* Static text for a status code. */
 const char* pa_status_string(int status);
 

@@ -73,6 +73,21 @@ def test_prefill_rejects(lib, kw, layout_kw, status):
     assert B.last_error()
 
 
+def test_window_argument_errors(lib):
+    layout = lay()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    st = lib.pa_prefill_window(*args, 1, 0.125, FAKE, FAKE, 1, 1, 600, -1, ctypes.byref(layout), None)
+    assert st == B.PA_ERR_INVALID_ARG
+    st = lib.pa_prefill_window(*args, 0, 0.125, FAKE, FAKE, 1, 1, 600, 16, ctypes.byref(layout), None)
+    assert st == B.PA_ERR_INVALID_ARG and "causal" in B.last_error()
+    st = lib.pa_prefill_window(*args, 1, 0.125, FAKE, FAKE, 0, 1, 600, 16, ctypes.byref(layout), None)
+    assert st == B.PA_OK
+    dl = B.make_layout(100, 16, 4, 128, 10)
+    need = lib.pa_decode_workspace_bytes(2, 4, ctypes.byref(dl))
+    st = lib.pa_decode_window(*args, 0.1, FAKE, 2, 4, -3, FAKE, need, ctypes.byref(dl), None)
+    assert st == B.PA_ERR_INVALID_ARG
+
+
 def test_prefill_empty_batch_is_ok_without_device(lib):
     assert prefill(lib, lay(), batch=0) == B.PA_OK
     assert prefill(lib, lay(), max_q_len=0) == B.PA_OK

@@ -343,3 +343,67 @@ def test_empty_batch_and_zero_rows_are_no_ops():
                         None)
     torch.cuda.synchronize()
     assert st == B.PA_OK and torch.all(out == 3.0)
+
+
+# ----------------------------------------------------------------- sliding window
+
+WINDOW_PREFILL_CASES = [
+    # (head_dim, page_size, lens, q_lens, window)
+    (128, 16, [300, 777], [300, 200], 1),
+    (128, 16, [300, 777], [300, 200], 50),
+    (128, 256, [1000, 129], [1000, 129], 64),
+    (128, 32, [513, 90], [400, 90], 200),
+    (64, 16, [259, 31], [259, 31], 17),
+    (128, 64, [700], [700], 5000),   # window longer than the sequence: no window
+]
+
+
+@pytest.mark.parametrize("d,ps,lens,q_lens,window", WINDOW_PREFILL_CASES)
+def test_prefill_sliding_window(d, ps, lens, q_lens, window):
+    G.banner(f"prefill window={window} d={d} ps={ps} lens={lens} q_lens={q_lens}")
+    wl = W.build("win", 300 + window, heads=3, head_dim=d, page_size=ps, lens=lens,
+                 q_lens=q_lens, causal=True, pool_slack=1.3, device="cuda", poison=True)
+    call = wl.calls[0]
+    out = torch.empty_like(call.q)
+    B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, True,
+                 wl.scale, out, call.q_start, call.max_q_len, window=window)
+    torch.cuda.synchronize()
+    from oracle import attention as OA
+    q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
+    ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, True,
+                              wl.scale, window=window)
+    G.compare(G.bf16_out_to_f64(out), ref, f"prefill window={window}")
+
+
+@pytest.mark.parametrize("window", [1, 7, 256, 1000, 100000])
+def test_decode_sliding_window(window):
+    G.banner(f"decode window={window}")
+    wl = W.build("wdec", 400 + window, heads=4, head_dim=128, page_size=16,
+                 lens=[1, 15, 300, 777, 3000], kind="decode", pool_slack=1.2, device="cuda",
+                 poison=True)
+    call = wl.calls[0]
+    out = torch.empty_like(call.q)
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale, out,
+                ws, window=window)
+    torch.cuda.synchronize()
+    from oracle import attention as OA
+    q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
+    ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, window=window)
+    G.compare(G.bf16_out_to_f64(out), ref, f"decode window={window}")
+
+
+def test_window_one_returns_own_value_row():
+    """w = 1: every query sees only its own key, so O is exactly its own V row."""
+    G.banner("window=1 exactness")
+    wl = W.build("w1", 77, heads=2, head_dim=128, page_size=16, lens=[333], q_lens=[100],
+                 causal=True, device="cuda", poison=True)
+    call = wl.calls[0]
+    out = torch.empty_like(call.q)
+    B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, True,
+                 wl.scale, out, call.q_start, call.max_q_len, window=1)
+    torch.cuda.synchronize()
+    bt = call.block_table_host[0]
+    for i in range(100):
+        t = 333 - 100 + i
+        assert torch.equal(out[i], wl.v_pool[int(bt[t // 16]), t % 16]), i

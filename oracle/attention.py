@@ -245,8 +245,31 @@ def paged_decode(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, scale:
     return out, lse
 
 
+def kv_append(k_pool_bits: np.ndarray, v_pool_bits: np.ndarray, block_table,
+              seq_ids: Sequence[int], positions: Sequence[int],
+              k_new_bits: np.ndarray, v_new_bits: np.ndarray):
+    """Writes new tokens' K/V rows into the paged pools (returns new pools).
+
+    "Flash Attention: Fast, Memory-Efficient Attention for LLMs", section "KV
+    Cache": each generated token's K_t, V_t are appended to the cache.  Token i
+    of sequence seq_ids[i] at absolute position positions[i] goes to the slot the
+    block table names for that position ("What is Paged FlashAttention?",
+    "Practical example").  k_new_bits, v_new_bits: uint16 [num_tokens, H_kv, d].
+    """
+    k = np.array(k_pool_bits, copy=True)
+    v = np.array(v_pool_bits, copy=True)
+    page_size = k.shape[1]
+    for i, (b, pos) in enumerate(zip(seq_ids, positions)):
+        _, offset, physical = locate_token(block_table[int(b)], int(pos), page_size)
+        if not 0 <= physical < k.shape[0]:
+            raise IndexError(f"token {i}: physical page {physical} outside the pool")
+        k[physical, offset] = k_new_bits[i]
+        v[physical, offset] = v_new_bits[i]
+    return k, v
+
+
 __all__ = [
     "bf16_to_f64", "pages_needed", "locate_token", "gather_sequence", "visible_mask",
     "scores", "softmax_rows", "weighted_values", "attend", "paged_prefill", "paged_decode",
-    "ROW_BLOCK",
+    "kv_append", "ROW_BLOCK",
 ]

@@ -413,6 +413,34 @@ def pin_sliding_window(seed=7) -> bool:
     return bool(np.max(np.abs(dec - pre[last_rows])) < 1e-14)
 
 
+def pin_kv_append_round_trip(seed=8) -> bool:
+    """Appending a sequence's K/V token by token into an empty (NaN) paged pool and
+    gathering it back returns exactly the appended rows; the worked example's token
+    300 lands in physical page 1, slot 44; no other slot changes."""
+    g = load_golden("paged_flashattention_practical_example.json")
+    ps, L, table = g["page_size"], g["seq_len"], g["block_table"]
+    rng = np.random.default_rng(seed)
+    heads, d, num_pages = 2, 4, 12
+    nan = np.uint16(0x7FC0)
+    k0 = np.full((num_pages, ps, heads, d), nan, dtype=np.uint16)
+    v0 = np.full((num_pages, ps, heads, d), nan, dtype=np.uint16)
+    kn = to_bf16_bits(rng.normal(size=(L, heads, d)))
+    vn = to_bf16_bits(rng.normal(size=(L, heads, d)))
+    order = rng.permutation(L)  # append order must not matter
+    k1, v1 = A.kv_append(k0, v0, [table], [0] * L, order, kn[order], vn[order])
+    if not np.array_equal(A.gather_sequence(k1, table, L, ps), A.bf16_to_f64(kn)):
+        return False
+    if not np.array_equal(A.gather_sequence(v1, table, L, ps), A.bf16_to_f64(vn)):
+        return False
+    for tok in g["tokens"]:
+        if not np.array_equal(k1[tok["physical_page"], tok["offset"]], kn[tok["token"]]):
+            return False
+    written = np.zeros((num_pages, ps), dtype=bool)
+    for j, phys in enumerate(table):
+        written[phys, :min(ps, L - j * ps)] = True
+    return bool(np.all(k1[~written] == nan) and np.all(v1[~written] == nan))
+
+
 ALL_PINS = [
     pin_practical_example_translation,
     pin_practical_example_gather,
@@ -425,6 +453,7 @@ ALL_PINS = [
     pin_rows_sum_to_one,
     pin_decode_matches_last_row,
     pin_sliding_window,
+    pin_kv_append_round_trip,
 ]
 
 

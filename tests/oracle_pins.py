@@ -14,6 +14,7 @@ import os
 import numpy as np
 
 from oracle import attention as A
+from oracle import logical_cache as LC
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -441,6 +442,74 @@ def pin_kv_append_round_trip(seed=8) -> bool:
     return bool(np.all(k1[~written] == nan) and np.all(v1[~written] == nan))
 
 
+def pin_logical_cache_fork_isolation(seed=9) -> bool:
+    """A fork starts with exactly the parent's first n rows; appends to the fork and to
+    the parent never show up in the other (copy on write); freeing one leaves the other
+    whole; lengths add up."""
+    rng = np.random.default_rng(seed)
+    heads, d = 2, 4
+    rows = lambda n: to_bf16_bits(rng.normal(size=(n, heads, d)))
+    cache = LC.LogicalCache(heads, d)
+    a_k, a_v = rows(10), rows(10)
+    cache.add(0)
+    cache.append(0, a_k[:4], a_v[:4])
+    cache.append(0, a_k[4:], a_v[4:])
+    cache.fork(0, 1, 6)
+    cache.fork(0, 2, 0)
+    b_k, b_v = rows(4), rows(4)
+    c_k, c_v = rows(3), rows(3)
+    cache.append(1, b_k, b_v)
+    cache.append(0, c_k, c_v)
+    k0, v0 = cache.rows(0)
+    k1, v1 = cache.rows(1)
+    ok = (np.array_equal(k0, np.concatenate([a_k, c_k])) and
+          np.array_equal(v0, np.concatenate([a_v, c_v])) and
+          np.array_equal(k1, np.concatenate([a_k[:6], b_k])) and
+          np.array_equal(v1, np.concatenate([a_v[:6], b_v])) and
+          cache.length(0) == 13 and cache.length(1) == 10 and cache.length(2) == 0)
+    cache.free(0)
+    k1b, v1b = cache.rows(1)
+    return bool(ok and np.array_equal(k1, k1b) and np.array_equal(v1, v1b)
+                and cache.live() == [1, 2])
+
+
+def pin_shared_prefix_pages_hold_both_sequences(seed=10) -> bool:
+    """The first page's shared-prefix example, paged: request 1 fills pages [3, 7, 12],
+    request 2 shares its first two pages and continues in page 9.  Writing both through
+    kv_append and gathering each through its own table gives each sequence's logical
+    rows; the page copy of copy on write moves every slot of a page and nothing else."""
+    g = load_golden("shared_prefix_block_tables.json")
+    t1, t2 = g["block_tables"]["request_1"], g["block_tables"]["request_2"]
+    shared = g["shared_prefix_blocks"]
+    rng = np.random.default_rng(seed)
+    ps, heads, d, num_pages = 4, 1, 4, 13
+    rows = lambda n: to_bf16_bits(rng.normal(size=(n, heads, d)))
+    nan = np.uint16(0x7FC0)
+    k = np.full((num_pages, ps, heads, d), nan, dtype=np.uint16)
+    v = k.copy()
+    cache = LC.LogicalCache(heads, d)
+    cache.add(1)
+    k1, v1 = rows(3 * ps - 1), rows(3 * ps - 1)
+    cache.append(1, k1, v1)
+    k, v = A.kv_append(k, v, [t1], [0] * len(k1), range(len(k1)), k1, v1)
+    cache.fork(1, 2, shared * ps)
+    k2, v2 = rows(3), rows(3)
+    cache.append(2, k2, v2)
+    pos2 = range(shared * ps, shared * ps + 3)
+    k, v = A.kv_append(k, v, [t1, t2], [1] * 3, pos2, k2, v2)
+    for seq, table in ((1, t1), (2, t2)):
+        L = cache.length(seq)
+        lk, lv = cache.rows(seq)
+        if not (np.array_equal(A.gather_sequence(k, table, L, ps), A.bf16_to_f64(lk)) and
+                np.array_equal(A.gather_sequence(v, table, L, ps), A.bf16_to_f64(lv))):
+            return False
+    ck, cv = LC.copy_pages(k, v, [t1[2]], [0])
+    untouched = [p for p in range(num_pages) if p != 0]
+    return bool(np.array_equal(ck[0], k[t1[2]]) and np.array_equal(cv[0], v[t1[2]]) and
+                np.array_equal(ck[untouched], k[untouched]) and
+                np.array_equal(cv[untouched], v[untouched]))
+
+
 ALL_PINS = [
     pin_practical_example_translation,
     pin_practical_example_gather,
@@ -454,6 +523,8 @@ ALL_PINS = [
     pin_decode_matches_last_row,
     pin_sliding_window,
     pin_kv_append_round_trip,
+    pin_logical_cache_fork_isolation,
+    pin_shared_prefix_pages_hold_both_sequences,
 ]
 
 

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 from oracle import attention as A
+from oracle import logical_cache as LC
 from tests import oracle_pins as P
 
 
@@ -75,8 +76,32 @@ def _wrong_bf16_shift(bits):
     return (bits.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
 
 
+def _fork_aliases_parent(self, parent, child, num_tokens):
+    # shares the parent's lists instead of starting new ones: no copy on write
+    self._k[child] = self._k[parent]
+    self._v[child] = self._v[parent]
+
+
+def _fork_drops_last_row(self, parent, child, num_tokens):
+    _ORIG_FORK(self, parent, child, max(0, num_tokens - 1))
+
+
+def _copy_pages_reversed(k_pool_bits, v_pool_bits, src_pages, dst_pages):
+    return _ORIG_COPY(k_pool_bits, v_pool_bits, dst_pages, src_pages)
+
+
+def _append_skips_v(k_pool_bits, v_pool_bits, block_table, seq_ids, positions, k_new, v_new):
+    k, _ = _ORIG["kv_append"](k_pool_bits, v_pool_bits, block_table, seq_ids, positions,
+                              k_new, v_new)
+    return k, np.array(v_pool_bits, copy=True)
+
+
+_ORIG_FORK = LC.LogicalCache.fork
+_ORIG_COPY = LC.copy_pages
+
 _ORIG = {name: getattr(A, name) for name in
-         ("locate_token", "visible_mask", "scores", "softmax_rows", "weighted_values", "bf16_to_f64")}
+         ("locate_token", "visible_mask", "scores", "softmax_rows", "weighted_values", "bf16_to_f64",
+          "kv_append")}
 
 MUTANTS = [
     ("locate_token", _swap_quotient_remainder),
@@ -91,12 +116,21 @@ MUTANTS = [
     ("softmax_rows", _softmax_sign_flip),
     ("weighted_values", _values_from_keys_layout),
     ("bf16_to_f64", _wrong_bf16_shift),
+    ("kv_append", _append_skips_v),
+    ("LogicalCache.fork", _fork_aliases_parent),
+    ("LogicalCache.fork", _fork_drops_last_row),
+    ("copy_pages", _copy_pages_reversed),
 ]
 
 
 @pytest.mark.parametrize("name,fn", MUTANTS, ids=[f"{n}:{f.__name__}" for n, f in MUTANTS])
 def test_some_pin_catches_mutant(monkeypatch, name, fn):
-    monkeypatch.setattr(A, name, fn)
+    if name == "LogicalCache.fork":
+        monkeypatch.setattr(LC.LogicalCache, "fork", fn)
+    elif name == "copy_pages":
+        monkeypatch.setattr(LC, name, fn)
+    else:
+        monkeypatch.setattr(A, name, fn)
     results = P.run_all_pins()
     assert not all(results.values()), f"no pin caught mutant {fn.__name__}: {results}"
 

@@ -24,11 +24,15 @@ PA_ERR_INVALID_ARG = 2
 PA_ERR_UNSUPPORTED = 3
 PA_ERR_WORKSPACE = 4
 PA_ERR_HIP = 5
+PA_ERR_CAPACITY = 6
 
 # Every symbol the header declares.
 EXPORTED = (
     "pa_prefill", "pa_decode_workspace_bytes", "pa_decode_split_tokens", "pa_decode",
     "pa_decode_partial", "pa_decode_combine", "pa_prefill_window", "pa_decode_window",
+    "pa_kv_append", "pa_copy_pages", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence",
+    "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append", "pa_bm_seq_len",
+    "pa_bm_free_page_count", "pa_bm_ref_count", "pa_bm_export", "pa_bm_validate",
     "pa_status_string", "pa_last_error", "pa_version",
 )
 
@@ -84,6 +88,33 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_prefill_window.restype = ctypes.c_int
     lib.pa_decode_window.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, vp, sz, lay, vp]
     lib.pa_decode_window.restype = ctypes.c_int
+    lib.pa_kv_append.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, lay, vp]
+    lib.pa_kv_append.restype = ctypes.c_int
+    lib.pa_copy_pages.argtypes = [vp, vp, vp, vp, i32, lay, vp]
+    lib.pa_copy_pages.restype = ctypes.c_int
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.pa_bm_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(vp)]
+    lib.pa_bm_create.restype = ctypes.c_int
+    lib.pa_bm_destroy.argtypes = [vp]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_add_sequence.argtypes = [vp, i32p]
+    lib.pa_bm_add_sequence.restype = ctypes.c_int
+    lib.pa_bm_fork.argtypes = [vp, i32, i32, i32p]
+    lib.pa_bm_fork.restype = ctypes.c_int
+    lib.pa_bm_free_sequence.argtypes = [vp, i32]
+    lib.pa_bm_free_sequence.restype = ctypes.c_int
+    lib.pa_bm_append.argtypes = [vp, i32, i32, i32p, i32p, i32p]
+    lib.pa_bm_append.restype = ctypes.c_int
+    lib.pa_bm_seq_len.argtypes = [vp, i32]
+    lib.pa_bm_seq_len.restype = i32
+    lib.pa_bm_free_page_count.argtypes = [vp]
+    lib.pa_bm_free_page_count.restype = i32
+    lib.pa_bm_ref_count.argtypes = [vp, i32]
+    lib.pa_bm_ref_count.restype = i32
+    lib.pa_bm_export.argtypes = [vp, vp, vp]
+    lib.pa_bm_export.restype = ctypes.c_int
+    lib.pa_bm_validate.argtypes = [vp]
+    lib.pa_bm_validate.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
@@ -247,3 +278,110 @@ def pa_decode_combine(seq_lens, out, workspace, layout: KVLayout, stream=None):
         _ptr(seq_lens), _ptr(out), out.shape[0], out.shape[1], _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(layout), _stream(stream))
     _check(st)
+
+
+def pa_kv_append(k_new, v_new, seq_ids, positions, k_pool, v_pool, block_table, stream=None):
+    """Writes the K/V rows of new tokens into their pages (in place); token i goes to
+    block_table[seq_ids[i], positions[i] // page_size], slot positions[i] % page_size."""
+    _check_device_tensors(k_new=k_new, v_new=v_new, seq_ids=seq_ids, positions=positions,
+                          k_pool=k_pool, v_pool=v_pool, block_table=block_table)
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _require(t.dtype == torch.bfloat16, f"{name} must be bfloat16")
+    for name, t in (("seq_ids", seq_ids), ("positions", positions), ("block_table", block_table)):
+        _require(t.dtype == torch.int32, f"{name} must be int32")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape, "k_pool/v_pool: [P, ps, Hkv, d]")
+    n = k_new.shape[0]
+    _require(k_new.shape == (n,) + tuple(k_pool.shape[2:]) and v_new.shape == k_new.shape,
+             "k_new/v_new: [num_tokens, Hkv, d]")
+    _require(seq_ids.numel() == n and positions.numel() == n, "seq_ids/positions: [num_tokens]")
+    _require(block_table.dim() == 2, "block_table: [num_seqs, maxp]")
+    lay = layout_of(k_pool, block_table)
+    _check(load_library().pa_kv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(seq_ids), _ptr(positions), n, _ptr(k_pool),
+        _ptr(v_pool), _ptr(block_table), block_table.shape[0], ctypes.byref(lay),
+        _stream(stream)))
+
+
+def pa_copy_pages(k_pool, v_pool, src_pages, dst_pages, stream=None):
+    """Copies page src_pages[i] to page dst_pages[i] in both pools (in place)."""
+    _check_device_tensors(k_pool=k_pool, v_pool=v_pool, src_pages=src_pages,
+                          dst_pages=dst_pages)
+    _require(k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
+             "pools must be bfloat16")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape, "k_pool/v_pool: [P, ps, Hkv, d]")
+    _require(src_pages.dtype == torch.int32 and dst_pages.dtype == torch.int32,
+             "src_pages/dst_pages must be int32")
+    _require(src_pages.numel() == dst_pages.numel(), "src_pages and dst_pages differ in length")
+    P, ps, hkv, d = k_pool.shape
+    lay = make_layout(P, ps, hkv, d, 1)
+    _check(load_library().pa_copy_pages(_ptr(k_pool), _ptr(v_pool), _ptr(src_pages),
+                                        _ptr(dst_pages), src_pages.numel(), ctypes.byref(lay),
+                                        _stream(stream)))
+
+
+class BlockManager:
+    """Host-side page manager of the library (pa_bm_* in pagedattn.h): block tables,
+    on-demand pages, reference counts and copy-on-write prefix sharing.  Touches no
+    device memory; the caller uploads the exported table and runs the page copies."""
+
+    def __init__(self, num_pages: int, page_size: int, max_seqs: int, max_pages_per_seq: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_bm_create(int(num_pages), int(page_size), int(max_seqs),
+                                      int(max_pages_per_seq), ctypes.byref(h)))
+        self._h = h
+        self.num_pages = int(num_pages)
+        self.page_size = int(page_size)
+        self.max_seqs = int(max_seqs)
+        self.max_pages_per_seq = int(max_pages_per_seq)
+
+    def close(self):
+        if self._h:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self) -> int:
+        s = ctypes.c_int32()
+        _check(self._lib.pa_bm_add_sequence(self._h, ctypes.byref(s)))
+        return s.value
+
+    def fork(self, parent: int, num_tokens: int) -> int:
+        c = ctypes.c_int32()
+        _check(self._lib.pa_bm_fork(self._h, int(parent), int(num_tokens), ctypes.byref(c)))
+        return c.value
+
+    def free_sequence(self, seq: int):
+        _check(self._lib.pa_bm_free_sequence(self._h, int(seq)))
+
+    def append(self, seq: int, num_tokens: int):
+        """Reserves num_tokens more tokens; returns the [(src, dst)] page copies to run."""
+        src, dst, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.pa_bm_append(self._h, int(seq), int(num_tokens), ctypes.byref(src),
+                                      ctypes.byref(dst), ctypes.byref(n)))
+        return [(src.value, dst.value)] if n.value else []
+
+    def seq_len(self, seq: int) -> int:
+        return int(self._lib.pa_bm_seq_len(self._h, int(seq)))
+
+    def free_page_count(self) -> int:
+        return int(self._lib.pa_bm_free_page_count(self._h))
+
+    def ref_count(self, page: int) -> int:
+        return int(self._lib.pa_bm_ref_count(self._h, int(page)))
+
+    def export(self):
+        """(block_table int32 [max_seqs, max_pages_per_seq], seq_lens int32 [max_seqs])."""
+        import numpy as np
+        table = np.empty((self.max_seqs, self.max_pages_per_seq), dtype=np.int32)
+        lens = np.empty(self.max_seqs, dtype=np.int32)
+        _check(self._lib.pa_bm_export(self._h, table.ctypes.data, lens.ctypes.data))
+        return table, lens
+
+    def validate(self):
+        _check(self._lib.pa_bm_validate(self._h))

@@ -6,13 +6,17 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 
 #include "kernels.h"
+#include "status.h"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
+
+namespace pa {
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -26,6 +30,13 @@ int ok() {
   g_last_error[0] = '\0';
   return PA_OK;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
 
 int log2_exact(int x) {
   int r = 0;
@@ -139,6 +150,8 @@ pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf1
   a.window = window;
   return a;
 }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
@@ -271,6 +284,66 @@ int pa_decode(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
                           num_q_heads, 0, workspace, workspace_bytes, layout, stream);
 }
 
+int pa_kv_append(const pa_bf16* k_new, const pa_bf16* v_new, const int32_t* seq_ids,
+                 const int32_t* positions, int32_t num_tokens, pa_bf16* k_pool,
+                 pa_bf16* v_pool, const int32_t* block_table, int32_t num_seqs,
+                 const pa_kv_layout* layout, hipStream_t stream) {
+  if (!layout) return fail(PA_ERR_NULL, "layout is NULL");
+  int st = check_layout(layout, layout->num_kv_heads);
+  if (st) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens=%d must be >= 0", num_tokens);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d must be >= 0", num_seqs);
+  if ((int64_t)layout->num_kv_heads * layout->head_dim > (int64_t)1 << 24)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads * head_dim exceeds 2^24");
+  if (!k_new || !v_new || !seq_ids || !positions || !k_pool || !v_pool || !block_table)
+    return fail(PA_ERR_NULL, "every array argument of pa_kv_append must be non-NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
+  if (num_tokens == 0 || num_seqs == 0) return ok();
+  pa::KvAppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.seq_ids = seq_ids;
+  a.positions = positions;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.num_pages = layout->num_pages;
+  a.log2_page_size = log2_exact(layout->page_size);
+  a.max_pages_per_seq = layout->max_pages_per_seq;
+  a.row_elems = layout->num_kv_heads * layout->head_dim;
+  return hip_status(pa::launch_kv_append(a, stream), "kv append launch");
+}
+
+int pa_copy_pages(pa_bf16* k_pool, pa_bf16* v_pool, const int32_t* src_pages,
+                  const int32_t* dst_pages, int32_t num_copies, const pa_kv_layout* layout,
+                  hipStream_t stream) {
+  if (!layout) return fail(PA_ERR_NULL, "layout is NULL");
+  int st = check_layout(layout, layout->num_kv_heads);
+  if (st) return st;
+  if (num_copies < 0) return fail(PA_ERR_INVALID_ARG, "num_copies=%d must be >= 0", num_copies);
+  const size_t page_bytes = (size_t)layout->page_size * layout->num_kv_heads *
+                            layout->head_dim * sizeof(pa_bf16);
+  if (page_bytes > ((size_t)1 << 28))
+    return fail(PA_ERR_INVALID_ARG, "a page of %zu bytes exceeds 256 MiB", page_bytes);
+  if (!k_pool || !v_pool || !src_pages || !dst_pages)
+    return fail(PA_ERR_NULL, "every array argument of pa_copy_pages must be non-NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_INVALID_ARG, "k_pool and v_pool must be 16-byte aligned");
+  if (num_copies == 0) return ok();
+  pa::CopyPagesArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.src_pages = src_pages;
+  a.dst_pages = dst_pages;
+  a.num_copies = num_copies;
+  a.num_pages = layout->num_pages;
+  a.page_bytes = page_bytes;
+  return hip_status(pa::launch_copy_pages(a, stream), "copy pages launch");
+}
+
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "PA_OK";
@@ -279,6 +352,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim or page_size not supported";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: decode workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
+    case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: no free page or sequence slot left";
     default: return "unknown pa_status";
   }
 }

@@ -49,6 +49,32 @@ struct DecodeArgs {
   int window;  // sliding-window length (0: none)
 };
 
+struct KvAppendArgs {
+  const uint16_t* k_new;  // [num_tokens, num_kv_heads, head_dim]
+  const uint16_t* v_new;
+  const int32_t* seq_ids;    // [num_tokens]
+  const int32_t* positions;  // [num_tokens]
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const int32_t* block_table;
+  int num_tokens;
+  int num_seqs;
+  int num_pages;
+  int log2_page_size;
+  int max_pages_per_seq;
+  int row_elems;  // num_kv_heads * head_dim (a multiple of 8)
+};
+
+struct CopyPagesArgs {
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const int32_t* src_pages;  // [num_copies]
+  const int32_t* dst_pages;  // [num_copies]
+  int num_copies;
+  int num_pages;
+  size_t page_bytes;  // page_size * num_kv_heads * head_dim * 2 (a multiple of 16)
+};
+
 // Rows of queries per prefill workgroup (4 waves x 32 rows) and keys per tile.
 constexpr int kPrefillBlockM = 128;
 constexpr int kPrefillBlockN = 64;
@@ -60,5 +86,7 @@ constexpr int kDecodeSplitTokens = 256;
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+hipError_t launch_copy_pages(const CopyPagesArgs& a, hipStream_t stream);
 
 }  // namespace pa

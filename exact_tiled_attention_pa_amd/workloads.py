@@ -106,6 +106,13 @@ def _normal_bf16(shape, sigma, gen, device, chunk=1 << 26):
     return out
 
 
+def normal_bf16(shape, sigma: float, seed: int, device) -> torch.Tensor:
+    """bf16 N(0, sigma^2) tensor from its own seeded generator on `device` (new K/V
+    rows for cache appends, fresh pools)."""
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    return _normal_bf16(tuple(shape), sigma, gen, device)
+
+
 def _pages_of(length: int, page_size: int) -> int:
     return -(-int(length) // int(page_size))
 

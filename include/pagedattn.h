@@ -27,9 +27,10 @@
  *   - bf16 values are passed as raw 16-bit patterns (pa_bf16).  Arithmetic is
  *     fp32 (MFMA accumulation, fp32 softmax state); outputs are rounded to
  *     bf16 round-to-nearest-even.
- *   - All array arguments are device pointers owned by the caller.  The library
- *     never allocates, frees or synchronises; work is enqueued asynchronously on
- *     the given HIP stream (0 = the null stream).
+ *   - All array arguments are device pointers owned by the caller (the block
+ *     manager's pa_bm_* calls are the exception: host memory only).  The library
+ *     never allocates device memory, frees or synchronises; work is enqueued
+ *     asynchronously on the given HIP stream (0 = the null stream).
  *   - Layouts are row-major:
  *       q, out          [tokens, num_q_heads, head_dim]
  *       k_pool, v_pool  [num_pages, page_size, num_kv_heads, head_dim]
@@ -47,7 +48,9 @@
  *   - Aliased physical pages (several sequences listing the same page, as with
  *     shared prefixes) are allowed: pools are only read.  out must not overlap
  *     any input.
- *   - Thread-safe: no global mutable state other than the thread-local error text.
+ *   - Thread-safe: no global mutable state other than the thread-local error text
+ *     (a block manager object is the caller's state and must not be shared between
+ *     threads without a lock).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -68,7 +71,8 @@ enum pa_status {
   PA_ERR_INVALID_ARG = 2,   /* a size or scalar is out of range */
   PA_ERR_UNSUPPORTED = 3,   /* valid but not implemented (head_dim, page_size) */
   PA_ERR_WORKSPACE = 4,     /* decode workspace missing or too small */
-  PA_ERR_HIP = 5            /* the HIP runtime reported an error at launch */
+  PA_ERR_HIP = 5,           /* the HIP runtime reported an error at launch */
+  PA_ERR_CAPACITY = 6       /* block manager: no free page or sequence slot left */
 };
 
 /* Shape of the paged KV pools.  Shared by K and V. */
@@ -180,6 +184,139 @@ int pa_decode_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_p
                      pa_bf16* out, int32_t batch, int32_t num_q_heads, int32_t window,
                      void* workspace, size_t workspace_bytes, const pa_kv_layout* layout,
                      hipStream_t stream);
+
+/*
+ * pa_kv_append -- write the K and V rows of new tokens into their pages, the step
+ * before attention in autoregressive decoding ([FA-LLM] "KV Cache": the new K_t,
+ * V_t join the cache, then the token attends over it).  Token i of sequence
+ * seq_ids[i] at absolute position positions[i] goes to physical page
+ * block_table[seq, pos / page_size], slot pos % page_size ([PFA] "Practical
+ * example"); every KV head of the token is written.
+ *
+ *   k_new, v_new  [num_tokens, num_kv_heads, head_dim] bf16 (device)
+ *   seq_ids       int32 [num_tokens] (device): row of block_table
+ *   positions     int32 [num_tokens] (device): absolute token position
+ *   k_pool, v_pool  pools described by layout; written in place
+ *   block_table   int32 [num_seqs, layout->max_pages_per_seq] (device)
+ *   num_tokens, num_seqs  >= 0 (0: nothing to do)
+ * A token whose seq id is outside [0, num_seqs), whose position is negative or
+ * at least max_pages_per_seq * page_size, or whose table entry is outside
+ * [0, num_pages) is skipped (its slot is not written), so a bad index never
+ * writes outside the pools.  Two tokens that map to the same slot race: which one
+ * lands is unspecified.  Pages read by other work on the stream must not be
+ * written concurrently (order the calls on one stream).  The layout's
+ * max_pages_per_seq is block_table's row length; num_q_heads plays no part.
+ * k_new, v_new and the pools must be 16-byte aligned (rows move in 16-byte pieces).
+ * Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ */
+int pa_kv_append(const pa_bf16* k_new, const pa_bf16* v_new, const int32_t* seq_ids,
+                 const int32_t* positions, int32_t num_tokens, pa_bf16* k_pool,
+                 pa_bf16* v_pool, const int32_t* block_table, int32_t num_seqs,
+                 const pa_kv_layout* layout, hipStream_t stream);
+
+/*
+ * pa_copy_pages -- copy whole pages of both pools, page src_pages[i] to page
+ * dst_pages[i]: the copy step of copy-on-write prefix sharing ([FA-PA] "How it
+ * works" under PagedAttention: sequences with a common prefix map it to the same
+ * physical blocks, and a shared block is copied before one of them writes into
+ * it).  Every slot of the page is copied, K and V.
+ *
+ *   src_pages, dst_pages  int32 [num_copies] (device)
+ *   num_copies            >= 0 (0: nothing to do)
+ * Pairs with an index outside [0, num_pages), or with src == dst, are skipped.
+ * No destination may appear twice or also appear as a source (the copies run
+ * concurrently).  The pools must be 16-byte aligned.  Errors: PA_ERR_NULL,
+ * PA_ERR_INVALID_ARG (page above 256 MiB, misaligned pool), PA_ERR_UNSUPPORTED,
+ * PA_ERR_HIP.
+ */
+int pa_copy_pages(pa_bf16* k_pool, pa_bf16* v_pool, const int32_t* src_pages,
+                  const int32_t* dst_pages, int32_t num_copies, const pa_kv_layout* layout,
+                  hipStream_t stream);
+
+/*
+ * Block manager: host-side bookkeeping of a paged pool shared by many sequences
+ * ([FA-PA] "How it works" under PagedAttention: fixed-size blocks handed out on
+ * demand, a block table per sequence, physical blocks shared between sequences with
+ * a common prefix and copied when one of them writes into a shared block; [PFA]
+ * "Practical example" for the mapping).  It allocates pages only as tokens arrive,
+ * counts the table entries naming each page, returns a page to the free list when
+ * its count drops to zero, and reports the page copies copy-on-write needs.
+ *
+ * Unlike the rest of this header these calls take and fill HOST memory and touch
+ * no device memory.  A manager is not thread-safe: serialise calls on one manager.
+ * Sequences are identified by their row in the exported block table
+ * (0 .. max_seqs - 1).  A failing call changes nothing.
+ *
+ * Typical step for a sequence s that grows by n tokens:
+ *   len = pa_bm_seq_len(bm, s);
+ *   pa_bm_append(bm, s, n, src, dst, &nc);       -- reserve pages, un-share
+ *   pa_copy_pages(k_pool, v_pool, src, dst, nc)  -- (src/dst uploaded to device)
+ *   pa_bm_export(bm, table, lens)                -- upload the table
+ *   pa_kv_append(..., positions len .. len+n-1)  -- write the new rows
+ *   pa_decode / pa_prefill over the exported table and lengths
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* Creates a manager of num_pages pages of page_size tokens for up to max_seqs
+ * sequences of up to max_pages_per_seq pages each; every page starts free.
+ * *out receives the manager (NULL on error).  Errors: PA_ERR_NULL,
+ * PA_ERR_INVALID_ARG (sizes < 1, or a table row mapping above 2^30 tokens),
+ * PA_ERR_CAPACITY (host memory). */
+int pa_bm_create(int32_t num_pages, int32_t page_size, int32_t max_seqs,
+                 int32_t max_pages_per_seq, pa_block_manager** out);
+
+/* Frees the manager (NULL is ignored). */
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* Starts an empty sequence; *seq_out receives its table row.  Errors: PA_ERR_NULL,
+ * PA_ERR_CAPACITY (every row in use). */
+int pa_bm_add_sequence(pa_block_manager* bm, int32_t* seq_out);
+
+/* Starts a sequence whose first num_tokens tokens are those of parent
+ * (0 <= num_tokens <= parent's length): it shares the parent's first
+ * ceil(num_tokens / page_size) pages, whose counts go up by one; no page is copied
+ * now.  *child_out receives its row.  Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG (parent
+ * not live, num_tokens out of range), PA_ERR_CAPACITY. */
+int pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t num_tokens,
+               int32_t* child_out);
+
+/* Ends a sequence: its table row is cleared and each of its pages loses one
+ * reference (pages reaching zero become free).  Errors: PA_ERR_NULL,
+ * PA_ERR_INVALID_ARG (not live). */
+int pa_bm_free_sequence(pa_block_manager* bm, int32_t seq);
+
+/* Grows seq by num_tokens >= 0 tokens, which will sit at positions len .. len+n-1.
+ * Allocates the pages those positions need.  If position len falls inside a page
+ * shared with another sequence, that page is replaced in seq's row by a fresh page
+ * and the pair (old, fresh) is written to copy_src[0], copy_dst[0] with
+ * *num_copies = 1 (else 0): the caller must copy it (pa_copy_pages) before writing
+ * the new tokens.  copy_src and copy_dst need room for one entry.  All or nothing:
+ * with too few free pages nothing changes.  Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG
+ * (not live, num_tokens < 0, length above max_pages_per_seq * page_size),
+ * PA_ERR_CAPACITY. */
+int pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t num_tokens, int32_t* copy_src,
+                 int32_t* copy_dst, int32_t* num_copies);
+
+/* Length of a live sequence, -1 otherwise (or for a NULL manager). */
+int32_t pa_bm_seq_len(const pa_block_manager* bm, int32_t seq);
+
+/* Number of free pages (-1 for a NULL manager). */
+int32_t pa_bm_free_page_count(const pa_block_manager* bm);
+
+/* Table entries naming page (0 if free), -1 if page is out of range. */
+int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t page);
+
+/* Copies the block table to block_table (host int32 [max_seqs, max_pages_per_seq],
+ * -1 where no page is mapped) and the lengths to seq_lens (host int32 [max_seqs],
+ * 0 for unused rows): the arrays pa_kv_append, pa_prefill and pa_decode take.
+ * Errors: PA_ERR_NULL. */
+int pa_bm_export(const pa_block_manager* bm, int32_t* block_table, int32_t* seq_lens);
+
+/* Checks the manager's invariants (every mapped entry in range, reference counts
+ * equal to the table entries naming each page, free list = pages with no
+ * reference, no stale entries past a sequence's pages).  PA_OK or
+ * PA_ERR_INVALID_ARG with the first violation in pa_last_error(). */
+int pa_bm_validate(const pa_block_manager* bm);
 
 /* Static text for a status code. */
 const char* pa_status_string(int status);

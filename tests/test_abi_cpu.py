@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.pa_version().decode().count(".") == 2
-    for st in range(6):
+    for st in range(7):
         assert lib.pa_status_string(st).decode().startswith("PA_")
     assert "unknown" in lib.pa_status_string(99).decode()
 
@@ -136,3 +136,38 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         B.pa_prefill(q, q, q, q, q, True, 0.1, q, q, 4)
+
+
+def test_kv_append_rejects(lib):
+    layout = B.make_layout(100, 16, 4, 128, 10)
+    call = lambda **kw: lib.pa_kv_append(
+        kw.get("k", FAKE), FAKE, FAKE, kw.get("pos", FAKE), kw.get("n", 3), FAKE,
+        kw.get("vp", FAKE), FAKE, kw.get("seqs", 2), ctypes.byref(kw.get("layout", layout)), None)
+    assert call(k=None) == B.PA_ERR_NULL
+    assert call(pos=None) == B.PA_ERR_NULL
+    assert call(vp=None) == B.PA_ERR_NULL
+    assert call(n=-1) == B.PA_ERR_INVALID_ARG
+    assert call(seqs=-1) == B.PA_ERR_INVALID_ARG
+    assert call(layout=B.make_layout(100, 12, 4, 128, 10)) == B.PA_ERR_UNSUPPORTED
+    assert call(layout=B.make_layout(100, 16, 4, 96, 10)) == B.PA_ERR_UNSUPPORTED
+    assert call(layout=B.make_layout(0, 16, 4, 128, 10)) == B.PA_ERR_INVALID_ARG
+    assert lib.pa_kv_append(FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 1, None, None) \
+        == B.PA_ERR_NULL
+    assert call(k=FAKE + 2) == B.PA_ERR_INVALID_ARG and "aligned" in B.last_error()
+    assert call(n=0) == B.PA_OK
+    assert call(seqs=0) == B.PA_OK
+
+
+def test_copy_pages_rejects(lib):
+    layout = B.make_layout(100, 16, 4, 128, 1)
+    call = lambda **kw: lib.pa_copy_pages(
+        kw.get("k", FAKE), FAKE, kw.get("src", FAKE), FAKE, kw.get("n", 3),
+        ctypes.byref(kw.get("layout", layout)), None)
+    assert call(k=None) == B.PA_ERR_NULL
+    assert call(src=None) == B.PA_ERR_NULL
+    assert call(n=-2) == B.PA_ERR_INVALID_ARG
+    assert call(layout=B.make_layout(100, 16, 4, 32, 1)) == B.PA_ERR_UNSUPPORTED
+    # 256 tokens x 8192 heads x 128 x 2 bytes = 512 MiB per page
+    assert call(layout=B.make_layout(4, 256, 8192, 128, 1)) == B.PA_ERR_INVALID_ARG
+    assert call(k=FAKE + 8) == B.PA_ERR_INVALID_ARG
+    assert call(n=0) == B.PA_OK

@@ -32,8 +32,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_pa_amd", "csrc")
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "device_util.h", "kernels.h"],
-    "prefill": ["prefill.hip", "device_util.h", "kernels.h"],
+    "decode_gqa": ["decode_gqa.hip", "device_util.h", "lds_tile.h", "kernels.h"],
+    "prefill": ["prefill.hip", "device_util.h", "lds_tile.h", "kernels.h"],
 }
+# file-name stem of each kernel's committed counter summary
+KERNEL_FILES = {"decode": "decode_partial_kernel", "decode_gqa": "decode_gqa_kernel",
+                "prefill": "prefill_kernel"}
 
 
 def log(msg):
@@ -82,8 +86,7 @@ def source_digest(kind: str) -> str:
 def recorded_traffic(kind: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None if absent or
     if the kernel sources changed since the counters were taken."""
-    kernel = "decode_partial_kernel" if kind == "decode" else "prefill_kernel"
-    path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
+    path = os.path.join(PROFILES, f"{KERNEL_FILES[kind]}.{workload}.traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -101,6 +104,15 @@ def recorded_traffic(kind: str, workload: str):
 
 
 # ------------------------------------------------------------------ GPU legs
+
+def decode_kind(wl) -> str:
+    """Which pass-1 decode kernel the library runs for this head layout."""
+    return "decode_gqa" if wl.num_q_heads // wl.heads >= 2 else "decode"
+
+
+def decode_kernel_name(wl) -> str:
+    return f"{KERNEL_FILES[decode_kind(wl)]}<{wl.head_dim}>"
+
 
 def timed_decode(wl, call, steps, warmup):
     import torch
@@ -201,6 +213,10 @@ def cpu_baseline_decode(wl, call, budget_s=15.0):
             sel = torch.as_tensor(pages.astype("int64"), device=wl.k_pool.device)
             k = W.to_host_bits(wl.k_pool.index_select(0, sel))
             v = W.to_host_bits(wl.v_pool.index_select(0, sel))
+            rep = wl.num_q_heads // wl.heads
+            if rep > 1:  # grouped heads: the oracle is per head, so K/V heads repeat
+                k = np.repeat(k, rep, axis=2)
+                v = np.repeat(v, rep, axis=2)
             table = np.full((1, n), -1, dtype=np.int64)
             table[0] = np.arange(n)
             t0 = time.perf_counter()
@@ -217,7 +233,7 @@ def cpu_baseline_decode(wl, call, budget_s=15.0):
         "kind": "oracle",
         "sample": f"oracle (NumPy fp64, 1 BLAS thread) on {len(seqs)} of {call.batch} "
                   f"decode sequences ({sum(int(call.seq_lens_host[b]) for b in seqs)} "
-                  f"tokens, all {wl.heads} heads) in {spent:.1f} s",
+                  f"tokens, all {wl.num_q_heads} query heads) in {spent:.1f} s",
     }
 
 
@@ -260,7 +276,8 @@ def cpu_baseline_prefill(wl, call, budget_s=15.0):
 
 # ------------------------------------------------------------------ rocprofv3 summaries
 
-KERNEL_TAGS = {"decode": "decode_partial_kernel", "prefill": "prefill_kernel<128, true>",
+KERNEL_TAGS = {"decode": "decode_partial_kernel", "decode_gqa": "decode_gqa_kernel",
+               "prefill": "prefill_kernel<128, true>",
                "prefill_noncausal": "prefill_kernel<128, false>"}
 
 
@@ -306,7 +323,7 @@ def summarize_traffic(fetch_dir, write_dir, kind, workload, out_path, command):
     fetch_kib, f_fac, n = res["FETCH_SIZE"]
     write_kib, w_fac, _ = res["WRITE_SIZE"]
     hbm = (fetch_kib * f_fac + write_kib * w_fac) * 1024
-    src = "decode" if kind == "decode" else "prefill"
+    src = kind if kind in KERNEL_SOURCES else "prefill"
     lines = [f"# HBM traffic per launch of {tag} on workload {workload}",
              f"# command (run twice, once per counter): {command}",
              "# each counter is scaled by (1 GiB / its reading for a plain 1 GiB device copy);",
@@ -396,19 +413,20 @@ def main():
         ms_step = wall / args.steps * 1e3
         split_avg = sum(split_ms) / len(split_ms)
         achieved = nbytes / (split_avg * 1e-3) / 1e9
-        traffic = recorded_traffic("decode", wl.name)
+        traffic = recorded_traffic(decode_kind(wl), wl.name)
         result.update({
             "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
             "unit": "GB/s",
             "ms_per_step": round(ms_step, 4),
-            "config": {"workload": wl.name, "batch": call.batch, "heads": wl.heads,
-                       "head_dim": wl.head_dim, "page_size": wl.page_size,
+            "config": {"workload": wl.name, "batch": call.batch, "heads": wl.num_q_heads,
+                       "kv_heads": wl.heads, "head_dim": wl.head_dim,
+                       "page_size": wl.page_size,
                        "total_tokens": int(call.seq_lens_host.sum()),
                        "kv_bytes_per_step": nbytes, "description": wl.description},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                         "kernel": "decode_partial_kernel<128>",
+                         "kernel": decode_kernel_name(wl),
                          "kernel_ms_avg": round(split_avg, 4),
                          "combine_ms_avg": round(sum(comb_ms) / len(comb_ms), 4)},
         })

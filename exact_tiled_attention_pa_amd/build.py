@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
-SOURCES = ["api.cpp", "block_manager.cpp", "prefill.hip", "decode.hip", "kv_cache.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "prefill.hip", "decode.hip", "decode_gqa.hip",
+           "kv_cache.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -293,6 +293,7 @@ void launch_partial(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_q_heads / a.num_kv_heads >= kGqaMinGroup) return launch_decode_partial_gqa(a, stream);
   if (a.head_dim == 128) launch_partial<128>(a, stream);
   else launch_partial<64>(a, stream);
   return hipGetLastError();

@@ -83,8 +83,13 @@ constexpr int kPrefillBlockN = 64;
 // fetched one per lane, so a split holds at most 64 chunks of 16 tokens).
 constexpr int kDecodeSplitTokens = 256;
 
+// Query heads per K/V head from which decode reads each K/V page once per group.
+constexpr int kGqaMinGroup = 2;
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
+// grouped K/V heads (num_q_heads / num_kv_heads >= kGqaMinGroup): same workspace
+hipError_t launch_decode_partial_gqa(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_copy_pages(const CopyPagesArgs& a, hipStream_t stream);

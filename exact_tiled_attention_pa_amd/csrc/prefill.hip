@@ -56,6 +56,7 @@
 
 #include "device_util.h"
 #include "kernels.h"
+#include "lds_tile.h"
 
 namespace pa {
 namespace {
@@ -65,11 +66,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int BM = kPrefillBlockM;  // 128 query rows per workgroup
 constexpr int BN = kPrefillBlockN;  // 64 key positions per tile
 constexpr int kRescaleThreshold = 8;
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int D>
 struct Geometry {
@@ -82,21 +78,6 @@ struct Geometry {
   static constexpr int kDB = D / 32;                       // 32-wide output blocks
   static constexpr int kStageOut = D + 8;                  // epilogue row stride (elements)
 };
-
-// XOR swizzles of the 16-byte chunks of LDS row r.
-//   K: chunk c of row r sits in slot c ^ (r mod chunks).
-//   V: chunk c of row r sits in slot c ^ v_swizzle(r mod 4).
-template <int D>
-__device__ __forceinline__ int k_swizzle(int r) { return r & (Geometry<D>::kChunks - 1); }
-template <int D>
-__device__ __forceinline__ int v_swizzle(int r) {
-  const int x = r & 3;
-  return D == 128 ? ((2 * x) ^ (8 * (x & 1))) : 2 * x;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
-}
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))

@@ -15,6 +15,8 @@ Workload shapes (one GPU each):
   decode_64        decode, 64 sequences x 1 query token, 32 heads, d=128,
                    lengths uniform on {512..8192}, 16-token pages, pool sized
                    exactly to the total context, pages a random permutation
+  decode_64_gqa8   decode_64's lengths and page layout with grouped heads: 64
+                   query heads over 8 K/V heads (8 query heads per K/V head)
   prefill_4096     prefill, 1 sequence, 32 heads, d=128, N=4096, identity table,
                    256-token pages; causal and non-causal variants
   prefill_32k      causal paged prefill, 1 sequence, 8 heads, d=128, N=32768,
@@ -68,7 +70,7 @@ class AttnCall:
 @dataclass
 class Workload:
     name: str
-    heads: int
+    heads: int                     # K/V heads stored in the pools
     head_dim: int
     page_size: int
     num_pages: int
@@ -79,6 +81,11 @@ class Workload:
     v_pool: torch.Tensor
     calls: List[AttnCall] = field(default_factory=list)
     description: str = ""
+    q_heads: int = 0               # query heads (0: same as heads)
+
+    @property
+    def num_q_heads(self) -> int:
+        return self.q_heads or self.heads
 
     def digest(self) -> str:
         """SHA-256 over every input buffer (host copies), for the record."""
@@ -167,7 +174,7 @@ def _make_call(kind, q, table, lens, q_lens, causal, device):
 def build(name: str, seed: int, heads: int, head_dim: int, page_size: int,
           lens, q_lens=None, causal=True, kind="prefill", sigma=1.0, pool_pages=None,
           table=None, shuffle=True, pool_slack=1.0, device="cpu", poison=False,
-          scale=None, description="", tensors=True) -> Workload:
+          scale=None, description="", tensors=True, q_heads=None) -> Workload:
     """Generic builder: one call over one pool.
 
     lens     KV length per sequence (L_b)
@@ -175,6 +182,7 @@ def build(name: str, seed: int, heads: int, head_dim: int, page_size: int,
     table    explicit block table rows (list of lists) instead of a drawn one
     shuffle  draw the page assignment from a random permutation (else identity order)
     tensors  False: lay out lengths and tables only (q and pools are left None)
+    q_heads  query heads (a multiple of heads, the K/V heads); default heads
     """
     cpu_gen = torch.Generator(device="cpu").manual_seed(seed)
     lens = [int(x) for x in lens]
@@ -200,7 +208,7 @@ def build(name: str, seed: int, heads: int, head_dim: int, page_size: int,
     if tensors:
         dev_gen = torch.Generator(device=device).manual_seed(seed)
         q_rows = sum(q_lens) if kind == "prefill" else batch
-        q = _normal_bf16((q_rows, heads, head_dim), sigma, dev_gen, device)
+        q = _normal_bf16((q_rows, q_heads or heads, head_dim), sigma, dev_gen, device)
         k_pool = _normal_bf16((num_pages, page_size, heads, head_dim), sigma, dev_gen, device)
         v_pool = _normal_bf16((num_pages, page_size, heads, head_dim), sigma, dev_gen, device)
     if poison and tensors:
@@ -212,7 +220,7 @@ def build(name: str, seed: int, heads: int, head_dim: int, page_size: int,
     return Workload(name=name, heads=heads, head_dim=head_dim, page_size=page_size,
                     num_pages=num_pages, max_pages_per_seq=tbl.shape[1], scale=scale,
                     sigma=sigma, k_pool=k_pool, v_pool=v_pool, calls=[call],
-                    description=description)
+                    description=description, q_heads=int(q_heads or heads))
 
 
 def prefill_600(device="cpu", poison=False, seed=1, tensors=True) -> Workload:
@@ -228,6 +236,17 @@ def decode_64(device="cpu", poison=False, seed=2, tensors=True) -> Workload:
     return build("decode_64", seed, heads=32, head_dim=128, page_size=16, lens=lens,
                  kind="decode", shuffle=True, device=device, poison=poison, tensors=tensors,
                  description="decode, 64 seqs, 32 heads, d=128, L~U{512..8192}, pages of 16")
+
+
+def decode_64_gqa8(device="cpu", poison=False, seed=2, tensors=True) -> Workload:
+    """decode_64's lengths and pages with grouped heads: 64 query heads share 8 K/V heads."""
+    g = torch.Generator(device="cpu").manual_seed(seed * 7919 + 1)
+    lens = torch.randint(512, 8193, (64,), generator=g).tolist()
+    return build("decode_64_gqa8", seed, heads=8, head_dim=128, page_size=16, lens=lens,
+                 kind="decode", shuffle=True, device=device, poison=poison, tensors=tensors,
+                 q_heads=64,
+                 description="decode, 64 seqs, 64 query heads over 8 K/V heads, d=128, "
+                             "L~U{512..8192}, pages of 16")
 
 
 def prefill_4096(device="cpu", poison=False, causal=True, seed=3, tensors=True) -> Workload:
@@ -289,6 +308,7 @@ def mixed_128x4(device="cpu", poison=False, seed=5, tensors=True) -> Workload:
 FULL_WORKLOADS = {
     "prefill_600": prefill_600,
     "decode_64": decode_64,
+    "decode_64_gqa8": decode_64_gqa8,
     "prefill_4096_causal": lambda **kw: prefill_4096(causal=True, **kw),
     "prefill_4096_noncausal": lambda **kw: prefill_4096(causal=False, **kw),
     "prefill_32k": prefill_32k,

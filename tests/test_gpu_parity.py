@@ -85,30 +85,36 @@ DECODE_CASES = [
     (128, 16, 4, 4, [1, 15, 16, 17, 511, 512, 513, 3000]),
     (128, 256, 2, 2, [1, 255, 256, 257, 1500]),
     (64, 16, 3, 3, [7, 1024, 2049]),
+    # grouped K/V heads (one page read serves the whole group)
     (128, 32, 8, 2, [100, 700]),
     (64, 64, 4, 1, [65, 1]),
+    (128, 16, 16, 2, [1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 3000]),
+    (128, 16, 64, 8, [1, 100, 2049]),
+    (128, 256, 4, 2, [1, 255, 256, 257, 1500]),
+    (64, 16, 12, 3, [7, 1024, 2049]),
+    (128, 16, 32, 1, [5, 600]),
+    (128, 32, 40, 1, [100, 700]),         # 40 heads per K/V head: blocks of 32 + 8
+    (64, 64, 71, 1, [65, 1, 2000]),       # 71 heads: blocks of 32 + 32 + 7
 ]
 
 
 @pytest.mark.parametrize("d,ps,hq,hkv,lens", DECODE_CASES)
 def test_decode_small_element_wise(d, ps, hq, hkv, lens):
     G.banner(f"decode small d={d} ps={ps} Hq={hq} Hkv={hkv} lens={lens}")
-    wl = W.build("small", 200 + d + ps, heads=hkv, head_dim=d, page_size=ps, lens=lens,
-                 kind="decode", pool_slack=1.2, device="cuda", poison=True)
+    wl = W.build("small", 200 + d + ps + hq, heads=hkv, head_dim=d, page_size=ps, lens=lens,
+                 kind="decode", pool_slack=1.2, device="cuda", poison=True, q_heads=hq)
     call = wl.calls[0]
-    if hq != hkv:
-        gen = torch.Generator(device="cuda").manual_seed(9)
-        call.q = torch.randn(len(lens), hq, d, generator=gen, device="cuda").to(torch.bfloat16)
     out = G.run_call(wl, call)
     torch.cuda.synchronize()
     G.compare(G.bf16_out_to_f64(out), oracle_grouped(wl, call, hq, hkv),
               f"decode d={d} ps={ps}")
 
 
-def test_decode_two_passes_equal_one_call():
-    G.banner("decode partial+combine vs pa_decode")
+@pytest.mark.parametrize("hq", [4, 16])
+def test_decode_two_passes_equal_one_call(hq):
+    G.banner(f"decode partial+combine vs pa_decode, Hq={hq}")
     wl = W.build("small", 5, heads=4, head_dim=128, page_size=16, lens=[40, 1300, 900],
-                 kind="decode", device="cuda", poison=True)
+                 kind="decode", device="cuda", poison=True, q_heads=hq)
     call = wl.calls[0]
     ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
     one = G.run_call(wl, call, workspace=ws)
@@ -121,6 +127,28 @@ def test_decode_two_passes_equal_one_call():
 
 
 # ----------------------------------------------------------------- full-size, sampled
+
+def test_decode_64_gqa8_sampled():
+    G.banner("decode_64_gqa8 full size (64 query heads over 8 K/V heads), 6 sequences")
+    wl = W.decode_64_gqa8(device="cuda", poison=True)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    lens = call.seq_lens_host
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 21, 40})
+    ref = oracle_grouped_seqs(wl, call, seqs)
+    G.compare(G.bf16_out_to_f64(out), ref, "decode_64_gqa8")
+
+
+def oracle_grouped_seqs(wl, call, seqs):
+    from oracle import attention as OA
+    q, k, v, table = G.host_inputs(wl, call, seqs)
+    rep = wl.num_q_heads // wl.heads
+    k = np.repeat(k, rep, axis=2)
+    v = np.repeat(v, rep, axis=2)
+    ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, seqs=seqs)
+    return ref
+
 
 def test_decode_64_sampled():
     G.banner("decode_64 full size, 8 sequences sampled (all heads)")
@@ -315,10 +343,10 @@ def test_poisoned_and_clean_pools_agree_bitwise():
 
 def test_constant_values_return_the_constant():
     G.banner("constant V")
-    for kind in ("prefill", "decode"):
+    for kind, hq in (("prefill", 2), ("decode", 2), ("decode", 16)):
         wl = W.build("c", 41, heads=2, head_dim=128, page_size=16, lens=[1, 500, 64],
                      q_lens=[1, 500, 10] if kind == "prefill" else None, kind=kind,
-                     device="cuda", poison=True)
+                     device="cuda", poison=True, q_heads=hq)
         used = torch.isfinite(wl.v_pool.float())
         wl.v_pool[used] = 1.75
         out = G.run_call(wl, wl.calls[0]).float()
@@ -375,12 +403,13 @@ def test_prefill_sliding_window(d, ps, lens, q_lens, window):
     G.compare(G.bf16_out_to_f64(out), ref, f"prefill window={window}")
 
 
-@pytest.mark.parametrize("window", [1, 7, 256, 1000, 100000])
-def test_decode_sliding_window(window):
-    G.banner(f"decode window={window}")
+@pytest.mark.parametrize("window,hq", [(1, 4), (7, 4), (256, 4), (1000, 4), (100000, 4),
+                                       (1, 16), (40, 16), (777, 16)])
+def test_decode_sliding_window(window, hq):
+    G.banner(f"decode window={window} Hq={hq}")
     wl = W.build("wdec", 400 + window, heads=4, head_dim=128, page_size=16,
                  lens=[1, 15, 300, 777, 3000], kind="decode", pool_slack=1.2, device="cuda",
-                 poison=True)
+                 poison=True, q_heads=hq)
     call = wl.calls[0]
     out = torch.empty_like(call.q)
     ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
@@ -389,8 +418,9 @@ def test_decode_sliding_window(window):
     torch.cuda.synchronize()
     from oracle import attention as OA
     q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
+    k, v = np.repeat(k, hq // 4, axis=2), np.repeat(v, hq // 4, axis=2)
     ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, window=window)
-    G.compare(G.bf16_out_to_f64(out), ref, f"decode window={window}")
+    G.compare(G.bf16_out_to_f64(out), ref, f"decode window={window} Hq={hq}")
 
 
 def test_window_one_returns_own_value_row():

@@ -66,6 +66,8 @@ int check_layout(const pa_kv_layout* layout, int32_t num_q_heads) {
                 layout->page_size);
   if ((int64_t)layout->max_pages_per_seq * layout->page_size > (int64_t)1 << 30)
     return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size exceeds 2^30 tokens");
+  if ((int64_t)layout->num_pages * layout->page_size > ((int64_t)1 << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "num_pages * page_size exceeds 2^31 - 1 token rows");
   return PA_OK;
 }
 

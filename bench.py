@@ -168,6 +168,115 @@ def timed_prefill(wl, call, steps, warmup):
     return wall, [e[0].elapsed_time(e[1]) for e in ev]
 
 
+def timed_launches(fn, steps, warmup):
+    """HIP-event durations (ms) of `steps` launches of fn on torch's current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [e[0].elapsed_time(e[1]) for e in ev]
+
+
+def _rate(nbytes_or_flops, ms, peak, unit, **extra):
+    avg = sum(ms) / len(ms)
+    scale = 1e9 if unit == "GB/s" else 1e12
+    achieved = nbytes_or_flops / (avg * 1e-3) / scale
+    return dict(extra, achieved=round(achieved, 2), unit=unit, peak=peak,
+                frac=round(achieved / peak, 4), kernel_ms_avg=round(avg, 4))
+
+
+def next_rows_summary(decode_wl, steps, warmup):
+    """Throughput of the rows beyond the core path, each against its own roofline:
+    grouped-head decode, KV append, page copy, sliding-window prefill and decode."""
+    import numpy as np
+    import torch
+    from exact_tiled_attention_pa_amd import binding as B
+    from exact_tiled_attention_pa_amd import workloads as W
+
+    res = {}
+    # f4, decode: the decode_64 batch with a 1024-token window
+    call = decode_wl.calls[0]
+    ws = B.decode_workspace(call.q, decode_wl.k_pool, call.block_table)
+    out = torch.empty_like(call.q)
+    w = 1024
+    ms = timed_launches(lambda: B.pa_decode(call.q, decode_wl.k_pool, decode_wl.v_pool,
+                                            call.block_table, call.seq_lens, decode_wl.scale,
+                                            out, ws, window=w), steps, warmup)
+    seen = np.minimum(call.seq_lens_host.astype(np.int64), w).sum()
+    nbytes = int(seen) * 2 * decode_wl.heads * decode_wl.head_dim * 2
+    res["window_decode"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+                                 workload=f"decode_64, window {w}",
+                                 kernel="decode_partial_kernel<128> + decode_combine_kernel<128>")
+    del ws, out
+
+    # f1: grouped heads
+    g = W.decode_64_gqa8(device="cuda")
+    gc = g.calls[0]
+    ws = B.decode_workspace(gc.q, g.k_pool, gc.block_table)
+    out = torch.empty_like(gc.q)
+    ms = timed_launches(lambda: B.pa_decode_partial(gc.q, g.k_pool, g.v_pool, gc.block_table,
+                                                    gc.seq_lens, g.scale, ws), steps, warmup)
+    res["gqa_decode"] = _rate(decode_kv_bytes(g, gc), ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+                              workload=g.name, kernel=decode_kernel_name(g))
+    del g, gc, ws, out
+
+    # f2: appending a 4096-token chunk of one sequence (32 K/V heads, d=128, pages of 16)
+    n_tok, heads, d, ps = 4096, 32, 128, 16
+    a = W.build("append_4096", 11, heads=heads, head_dim=d, page_size=ps, lens=[n_tok],
+                kind="decode", pool_slack=1.25, device="cuda")
+    ac = a.calls[0]
+    k_new = W.normal_bf16((n_tok, heads, d), 1.0, 12, "cuda")
+    v_new = W.normal_bf16((n_tok, heads, d), 1.0, 13, "cuda")
+    ids = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
+    pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
+    ms = timed_launches(lambda: B.pa_kv_append(k_new, v_new, ids, pos, a.k_pool, a.v_pool,
+                                               ac.block_table), steps, warmup)
+    nbytes = n_tok * heads * d * 2 * 2 * 2  # K and V rows, read once and written once
+    res["kv_append"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+                             workload="append_4096: 4096 tokens, 32 K/V heads, d=128, "
+                                      "pages of 16, shuffled", kernel="kv_append_kernel")
+
+    del a, ac, k_new, v_new, ids, pos
+
+    # f3: copy-on-write page copies: 2048 disjoint page pairs in a 4096-page pool
+    n_pages, n_pairs = 4096, 2048
+    kp = W.normal_bf16((n_pages, ps, heads, d), 1.0, 14, "cuda")
+    vp = W.normal_bf16((n_pages, ps, heads, d), 1.0, 15, "cuda")
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(16))
+    src = perm[:n_pairs].to(torch.int32).cuda()
+    dst = perm[n_pairs:2 * n_pairs].to(torch.int32).cuda()
+    ms = timed_launches(lambda: B.pa_copy_pages(kp, vp, src, dst), steps, warmup)
+    page_bytes = ps * heads * d * 2
+    nbytes = n_pairs * page_bytes * 2 * 2  # both pools, read and write
+    res["copy_pages"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+                              workload=f"copy_2048: {n_pairs} page pairs of 16 tokens x 32 "
+                                       "heads x d=128", kernel="copy_pages_kernel")
+    del kp, vp, src, dst
+
+    # f4, prefill: prefill_32k with a 4096-token window
+    p = W.prefill_32k(device="cuda")
+    pc = p.calls[0]
+    out = torch.empty_like(pc.q)
+    w = 4096
+    ms = timed_launches(lambda: B.pa_prefill(pc.q, p.k_pool, p.v_pool, pc.block_table,
+                                             pc.seq_lens, True, p.scale, out, pc.q_start,
+                                             pc.max_q_len, window=w), steps, warmup)
+    n = int(pc.seq_lens_host[0])
+    pairs = w * (w + 1) // 2 + (n - w) * w
+    flops = 4 * p.head_dim * pc.q.shape[1] * pairs
+    res["window_prefill"] = _rate(flops, ms, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
+                                  workload=f"prefill_32k, window {w}", kernel="prefill_kernel")
+    del p, pc, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_summary(wl, call, steps, warmup):
     flops, nbytes = prefill_work(wl, call)
     wall, ms = timed_prefill(wl, call, steps, warmup)
@@ -357,6 +466,8 @@ def main():
     ap.add_argument("--prefill-workload", default="prefill_4096_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the grouped-head / append / copy / window legs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
@@ -442,6 +553,9 @@ def main():
             t_meas = (split_avg + sum(comb_ms) / len(comb_ms) + cs["kernel_ms_avg"]) * 1e-3
             result["chunks"] = cs
             result["combined_roofline_fraction"] = round(t_roof / t_meas, 4)
+        if not args.no_next and len(wl.calls) == 1 and wl.name == "decode_64":
+            log("rows beyond the core path: grouped heads, append, page copy, windows")
+            result["next_rows"] = next_rows_summary(wl, args.steps, args.warmup)
     else:
         s = prefill_summary(wl, call, args.steps, args.warmup)
         result.update({

@@ -437,3 +437,67 @@ def test_window_one_returns_own_value_row():
     for i in range(100):
         t = 333 - 100 + i
         assert torch.equal(out[i], wl.v_pool[int(bt[t // 16]), t % 16]), i
+
+
+# ----------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("causal,hq", [(True, 2), (False, 2), (True, 4)])
+def test_prefill_ragged_batch_with_empty_chunks(causal, hq):
+    """Sequences with no query rows in the middle of a batch, a one-row chunk on a long
+    cache, a chunk that is the whole sequence: rows past each chunk are never written."""
+    G.banner(f"prefill ragged batch with empty chunks causal={causal} Hq={hq}")
+    lens, q_lens = [10, 5, 7, 300, 64, 1], [0, 5, 0, 300, 1, 1]
+    wl = W.build("rag", 61, heads=2, head_dim=128, page_size=16, lens=lens, q_lens=q_lens,
+                 causal=causal, pool_slack=1.3, device="cuda", poison=True, q_heads=hq)
+    call = wl.calls[0]
+    out = torch.full_like(call.q, float("nan"))
+    B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, causal,
+                 wl.scale, out, call.q_start, call.max_q_len)
+    torch.cuda.synchronize()
+    ref = oracle_grouped(wl, call, hq, 2)
+    G.compare(G.bf16_out_to_f64(out), ref, f"ragged causal={causal} Hq={hq}")
+
+
+def test_zero_scale_averages_the_visible_values():
+    """scale = 0: every visible key gets the same weight, so O is the mean of the
+    visible V rows (causal prefill: a running mean; decode: the mean of the cache)."""
+    G.banner("scale 0")
+    for kind in ("prefill", "decode"):
+        wl = W.build("z", 71, heads=2, head_dim=128, page_size=16, lens=[1, 333, 70],
+                     q_lens=[1, 333, 20] if kind == "prefill" else None, kind=kind,
+                     device="cuda", poison=True, scale=0.0)
+        call = wl.calls[0]
+        out = G.run_call(wl, call)
+        torch.cuda.synchronize()
+        G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), f"scale 0 {kind}")
+
+
+def test_prefill_window_grouped_heads():
+    G.banner("prefill window=100 with 8 query heads over 2 K/V heads")
+    wl = W.build("wg", 81, heads=2, head_dim=128, page_size=32, lens=[777, 300],
+                 q_lens=[500, 300], causal=True, pool_slack=1.2, device="cuda", poison=True,
+                 q_heads=8)
+    call = wl.calls[0]
+    out = torch.empty_like(call.q)
+    B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, True,
+                 wl.scale, out, call.q_start, call.max_q_len, window=100)
+    torch.cuda.synchronize()
+    from oracle import attention as OA
+    q, k, v, table = G.host_inputs(wl, call, [0, 1])
+    k, v = np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2)
+    ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, True,
+                              wl.scale, window=100)
+    G.compare(G.bf16_out_to_f64(out), ref, "prefill window=100 grouped")
+
+
+@pytest.mark.parametrize("hq", [1, 4])
+def test_decode_half_million_token_sequence(hq):
+    """A 524,288-token sequence (2048 splits merged by the combine pass) next to a
+    one-token one, pages of 256 shuffled over the pool."""
+    G.banner(f"decode L=524288 Hq={hq}")
+    wl = W.build("long", 91, heads=1, head_dim=128, page_size=256, lens=[524288, 1],
+                 kind="decode", device="cuda", poison=True, q_heads=hq, sigma=0.5)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), oracle_grouped(wl, call, hq, 1), f"decode long Hq={hq}")

@@ -77,25 +77,30 @@ int check_scale(float scale) {
   return PA_OK;
 }
 
-int split_tokens_of(const pa_kv_layout* layout) {
+// Keys per decode split: grouped heads walk longer splits (their workgroups read a
+// quarter of the bytes per key that one-head-per-row workgroups do, so a longer split
+// keeps the per-workgroup set-up and merge small against the streaming).
+int split_tokens_of(const pa_kv_layout* layout, int32_t num_q_heads) {
+  if (num_q_heads / layout->num_kv_heads >= pa::kGqaMinGroup)
+    return pa::kDecodeSplitTokensGrouped;
   return layout->page_size > pa::kDecodeSplitTokens ? layout->page_size
                                                      : pa::kDecodeSplitTokens;
 }
 
-int max_splits_of(const pa_kv_layout* layout) {
+int max_splits_of(const pa_kv_layout* layout, int32_t num_q_heads) {
   const int64_t tokens = (int64_t)layout->max_pages_per_seq * layout->page_size;
-  const int st = split_tokens_of(layout);
+  const int st = split_tokens_of(layout, num_q_heads);
   return (int)((tokens + st - 1) / st);
 }
 
 // Workspace: fp32 O partials first, then (m, l) pairs, each region 256-byte aligned.
 size_t ws_o_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
-  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout) * layout->head_dim;
+  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout, num_q_heads) * layout->head_dim;
   return (n * sizeof(float) + 255) / 256 * 256;
 }
 
 size_t ws_ml_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
-  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout) * 2;
+  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout, num_q_heads) * 2;
   return (n * sizeof(float) + 255) / 256 * 256;
 }
 
@@ -114,7 +119,7 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
     if (st) return st;
   }
   if (!seq_lens) return fail(PA_ERR_NULL, "seq_lens must be non-NULL");
-  if (max_splits_of(layout) > 65535)
+  if (max_splits_of(layout, num_q_heads) > 65535)
     return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size = %lld needs more than 65535 "
                 "decode splits", (long long)layout->max_pages_per_seq * layout->page_size);
   const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
@@ -147,8 +152,8 @@ pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf1
   a.head_dim = layout->head_dim;
   a.log2_page_size = log2_exact(layout->page_size);
   a.max_pages_per_seq = layout->max_pages_per_seq;
-  a.split_tokens = split_tokens_of(layout);
-  a.max_splits = max_splits_of(layout);
+  a.split_tokens = split_tokens_of(layout, num_q_heads);
+  a.max_splits = max_splits_of(layout, num_q_heads);
   a.window = window;
   return a;
 }
@@ -228,10 +233,9 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
   return ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
 }
 
-int32_t pa_decode_split_tokens(const pa_kv_layout* layout) {
-  if (!layout || log2_exact(layout->page_size) < 4 || log2_exact(layout->page_size) > 8)
-    return 0;
-  return split_tokens_of(layout);
+int32_t pa_decode_split_tokens(int32_t num_q_heads, const pa_kv_layout* layout) {
+  if (check_layout(layout, num_q_heads) != PA_OK) return 0;
+  return split_tokens_of(layout, num_q_heads);
 }
 
 int pa_decode_partial(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,

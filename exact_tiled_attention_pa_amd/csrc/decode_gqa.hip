@@ -113,6 +113,14 @@ decode_gqa_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     for (int j = 0; j < G::kDK; ++j) qf[j] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 
+  // Physical page of each 16-token group of the split, one group per lane, fetched with
+  // one vector load: the tile loads then find their pages with v_readlane instead of
+  // waiting for a scalar load of the table before each group.
+  static_assert(kDecodeSplitTokensGrouped / 16 <= 64, "a split's groups fit in one wave");
+  int group_page = 0;
+  if (lane < (t_end - t_begin + 15) / 16)
+    group_page = bt[min((t_begin + 16 * lane) >> log2_ps, last_page)];
+
   // Loads: instruction i fills tile rows kRowsPerInst*i + lane/chunks, slot lane%chunks.
   // The row's place in its 16-row group and its swizzle repeat every kInstPerGroup
   // instructions, so kInstPerGroup byte offsets per lane serve every load.
@@ -159,7 +167,7 @@ decode_gqa_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     for (int i = 0; i < G::kInstPerTile; ++i) {
       const int first_row = G::kRowsPerInst * i;
       const int t0 = kt0 + (first_row & ~15);
-      const int phys = bt[min(t0 >> log2_ps, last_page)];
+      const int phys = __builtin_amdgcn_readlane(group_page, (t0 - t_begin) >> 4);
       const int valid = min(16, t_end - t0);
       const int bytes = valid > 0 ? valid * row_bytes_g : 0;
       const size_t elem =

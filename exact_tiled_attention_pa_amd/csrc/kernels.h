@@ -82,9 +82,11 @@ constexpr int kPrefillBlockN = 64;
 // Keys per decode split when pages are at most this long (a split's chunk pages are
 // fetched one per lane, so a split holds at most 64 chunks of 16 tokens).
 constexpr int kDecodeSplitTokens = 256;
+// Keys per decode split with grouped heads (at most 64 groups of 16 keys).
+constexpr int kDecodeSplitTokensGrouped = 1024;
 
 // Query heads per K/V head from which decode reads each K/V page once per group.
-constexpr int kGqaMinGroup = 2;
+constexpr int kGqaMinGroup = 4;
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);

@@ -124,8 +124,10 @@ int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                  const pa_kv_layout* layout);
 
-/* Key positions covered by one decode split (a multiple of page_size). */
-int32_t pa_decode_split_tokens(const pa_kv_layout* layout);
+/* Key positions covered by one decode split (a multiple of page_size): 256 (or
+ * page_size, if larger) when each query head has its own K/V head, 1024 when
+ * num_q_heads / num_kv_heads >= 4.  0 for an invalid layout or head count. */
+int32_t pa_decode_split_tokens(int32_t num_q_heads, const pa_kv_layout* layout);
 
 /*
  * pa_decode -- one new query token per sequence attending over all L_b cached

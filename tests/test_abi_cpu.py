@@ -97,15 +97,25 @@ def test_prefill_empty_batch_is_ok_without_device(lib):
 def test_decode_workspace_size_formula(lib):
     layout = B.make_layout(17000, 16, 32, 128, 512)
     # 512 pages x 16 tokens, 256-token splits -> 32 splits per sequence
-    assert lib.pa_decode_split_tokens(ctypes.byref(layout)) == 256
+    assert lib.pa_decode_split_tokens(32, ctypes.byref(layout)) == 256
     o = 64 * 32 * 32 * 128 * 4
     ml = 64 * 32 * 32 * 2 * 4
     r = lambda n: (n + 255) // 256 * 256
     assert lib.pa_decode_workspace_bytes(64, 32, ctypes.byref(layout)) == r(o) + r(ml)
     big = B.make_layout(128, 256, 8, 128, 128)
-    assert lib.pa_decode_split_tokens(ctypes.byref(big)) == 256
+    assert lib.pa_decode_split_tokens(8, ctypes.byref(big)) == 256
     bad = B.make_layout(128, 24, 8, 128, 128)
     assert lib.pa_decode_workspace_bytes(1, 8, ctypes.byref(bad)) == 0
+    assert lib.pa_decode_split_tokens(8, ctypes.byref(bad)) == 0
+    # grouped heads: 8 K/V heads, 2 query heads each keep 256-token splits; 4 or more
+    # per K/V head walk 1024-token splits -> 8 splits of 8192 tokens
+    gl = B.make_layout(17000, 16, 8, 128, 512)
+    assert lib.pa_decode_split_tokens(16, ctypes.byref(gl)) == 256
+    assert lib.pa_decode_split_tokens(64, ctypes.byref(gl)) == 1024
+    assert lib.pa_decode_split_tokens(12, ctypes.byref(gl)) == 0  # not a multiple of 8
+    o = 64 * 64 * 8 * 128 * 4
+    ml = 64 * 64 * 8 * 2 * 4
+    assert lib.pa_decode_workspace_bytes(64, 64, ctypes.byref(gl)) == r(o) + r(ml)
 
 
 def test_decode_rejects(lib):

@@ -468,6 +468,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the grouped-head / append / copy / window legs")
+    ap.add_argument("--only-next", action="store_true",
+                    help="run only those legs (on the decode_64 batch) and print them")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
@@ -509,6 +511,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.only_next:
+        wl = W.decode_64(device="cuda")
+        print(json.dumps({"next_rows": next_rows_summary(wl, args.steps, args.warmup)}),
+              flush=True)
+        return
 
     if args.workload not in W.FULL_WORKLOADS:
         raise SystemExit(f"unknown workload {args.workload}")

@@ -501,3 +501,51 @@ def test_decode_half_million_token_sequence(hq):
     out = G.run_call(wl, call)
     torch.cuda.synchronize()
     G.compare(G.bf16_out_to_f64(out), oracle_grouped(wl, call, hq, 1), f"decode long Hq={hq}")
+
+
+# ----------------------------------------------------------------- kernel against kernel
+
+def test_grouped_decode_kernel_agrees_with_per_head_kernel():
+    """The same attention computed by the two decode kernels: 8 query heads over 2 K/V
+    heads (grouped kernel) and over 8 K/V heads holding copies of those 2 (one K/V head
+    per query head, the per-head kernel).  Both meet the oracle bar; they differ only by
+    rounding order, so they agree to well within it."""
+    G.banner("grouped vs per-head decode kernels")
+    lens = [1, 300, 2500, 1025]
+    wl = W.build("ab", 13, heads=2, head_dim=128, page_size=16, lens=lens, kind="decode",
+                 pool_slack=1.2, device="cuda", poison=True, q_heads=8)
+    call = wl.calls[0]
+    grouped = G.run_call(wl, call)
+    k_rep = wl.k_pool.repeat_interleave(4, dim=2).contiguous()
+    v_rep = wl.v_pool.repeat_interleave(4, dim=2).contiguous()
+    out = torch.empty_like(call.q)
+    ws = B.decode_workspace(call.q, k_rep, call.block_table)
+    B.pa_decode(call.q, k_rep, v_rep, call.block_table, call.seq_lens, wl.scale, out, ws)
+    torch.cuda.synchronize()
+    ref = oracle_grouped(wl, call, 8, 2)
+    G.compare(G.bf16_out_to_f64(grouped), ref, "grouped kernel")
+    G.compare(G.bf16_out_to_f64(out), ref, "per-head kernel")
+    G.compare(G.bf16_out_to_f64(grouped), G.bf16_out_to_f64(out), "grouped vs per-head",
+              max_tol=8e-3, mean_tol=5e-4)
+
+
+@pytest.mark.parametrize("hq", [4, 16])
+def test_decode_agrees_with_last_prefill_row(hq):
+    """Decode (split-K VALU or grouped MFMA kernel plus the combine pass) and the last row
+    of a causal prefill (tiled MFMA kernel) over the same cache compute the same thing."""
+    G.banner(f"decode vs last prefill row Hq={hq}")
+    lens = [1, 64, 257, 3000]
+    wl = W.build("dp", 17, heads=4, head_dim=128, page_size=16, lens=lens, q_lens=lens,
+                 causal=True, pool_slack=1.2, device="cuda", poison=True, q_heads=hq)
+    call = wl.calls[0]
+    pre = G.run_call(wl, call)
+    last = torch.tensor([int(call.q_start_host[b + 1]) - 1 for b in range(len(lens))],
+                        device="cuda")
+    q_dec = call.q.index_select(0, last).contiguous()
+    out = torch.empty_like(q_dec)
+    ws = B.decode_workspace(q_dec, wl.k_pool, call.block_table)
+    B.pa_decode(q_dec, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale, out,
+                ws)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), G.bf16_out_to_f64(pre.index_select(0, last)),
+              "decode vs prefill last row", max_tol=8e-3, mean_tol=5e-4)

@@ -95,6 +95,8 @@ DECODE_CASES = [
     (128, 16, 32, 1, [5, 600]),
     (128, 32, 40, 1, [100, 700]),         # 40 heads per K/V head: blocks of 32 + 8
     (64, 64, 71, 1, [65, 1, 2000]),       # 71 heads: blocks of 32 + 32 + 7
+    (128, 256, 16, 2, [1, 255, 256, 257, 1023, 1024, 1025, 5000]),
+    (64, 128, 8, 1, [127, 128, 129, 2049]),
 ]
 
 

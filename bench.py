@@ -464,6 +464,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_64")
     ap.add_argument("--prefill-workload", default="prefill_4096_causal")
+    ap.add_argument("--prefill-long-workload", default="prefill_32k",
+                    help="second prefill leg: the long causal context")
+    ap.add_argument("--no-prefill-long", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-next", action="store_true",
@@ -581,6 +584,13 @@ def main():
         # a longer warm-up: the leg follows the decode loop and must not time clock ramps
         result["prefill"] = prefill_summary(pw, pw.calls[0], args.steps, max(args.warmup, 10))
         del pw
+        if not args.no_prefill_long:
+            log(f"prefill leg: {args.prefill_long_workload}")
+            pw = W.FULL_WORKLOADS[args.prefill_long_workload](device="cuda")
+            result["prefill_long"] = prefill_summary(pw, pw.calls[0], min(args.steps, 10),
+                                                     max(args.warmup, 3))
+            del pw
+            torch.cuda.empty_cache()
 
     # the oracle runs last, after every GPU leg, so its host time cannot idle the GPU
     # between a warm-up and a timed region

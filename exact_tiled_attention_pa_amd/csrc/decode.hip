@@ -14,10 +14,13 @@
 //     head groups of the same key range, so concurrently running workgroups read
 //     adjacent kilobytes of the same token rows (DRAM row locality), instead of
 //     256-byte pieces 8 KB apart.  A split is a range of split_tokens key
-//     positions (whole pages); its keys come in 16-token chunks and each of the 4
-//     waves takes 4 consecutive tokens of every chunk, straight into registers,
-//     two chunks ahead of the one being consumed.  The physical page of every
-//     chunk comes from the block table ("What is Paged FlashAttention?",
+//     positions (whole pages).  Its keys are streamed in steps of 16 tokens, each
+//     of the 4 waves taking 4 consecutive tokens of a step, with buffer loads that
+//     write straight into a per-wave ring of LDS slots (no VGPR staging, so the
+//     kernel needs few registers and the ring, not the register file, sets how
+//     many bytes are in flight: 4 steps = 32 KB per wave, 128 KB per CU).  Each
+//     lane reads its own 16 bytes back from LDS.  The physical page of every
+//     16-token chunk comes from the block table ("What is Paged FlashAttention?",
 //     "Practical example"), fetched for the whole split by one vector load.
 //     Dot products run on the VALU and are summed over the 16 lanes of a head
 //     with DPP moves; every 16-lane row group keeps its own online-softmax state
@@ -34,6 +37,7 @@
 
 #include "device_util.h"
 #include "kernels.h"
+#include "lds_tile.h"
 
 namespace pa {
 namespace {
@@ -41,7 +45,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 16;                   // tokens per chunk (never straddles a page)
-constexpr int kTokPerWave = kChunk / kWaves; // consecutive tokens of a chunk per wave
+constexpr int kStep = kChunk / kWaves;       // consecutive tokens of a chunk per wave
+constexpr int kRing = 5;                     // LDS slots per wave: 4 steps in flight
+constexpr int kSlotBytes = kStep * 2 * 1024; // the step's K rows, then its V rows
 constexpr float kEmptyMax = -1e30f;          // running max before any visible key (finite)
 
 template <int D>
@@ -60,9 +66,12 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       int num_kv_heads, int log2_ps, int max_pages, int split_tokens,
                       int max_splits, int window) {
   using G = DecodeGeometry<D>;
-  __shared__ float sm_o[kWaves][G::kHeads][D];
-  __shared__ float sm_m[kWaves][G::kHeads];
-  __shared__ float sm_l[kWaves][G::kHeads];
+  constexpr int kRingBytes = kWaves * kRing * kSlotBytes;  // 160 KB: one workgroup per CU
+  constexpr int kMergeBytes = (kWaves * G::kHeads * D + 2 * kWaves * G::kHeads) * 4;
+  static_assert(kMergeBytes <= kRingBytes, "the merge arrays reuse the ring");
+  constexpr uint32_t kOutside = 0x80000000u;   // a load offset past every buffer
+  constexpr uint32_t kAllBytes = 0x7fffffffu;  // buffer size: offsets are checked here
+  __shared__ __attribute__((aligned(1024))) char ring[kRingBytes];
 
   const int hg = blockIdx.x;
   const int split = blockIdx.y;
@@ -84,7 +93,9 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const bool active = h < num_q_heads;
   const int hk = (active ? h : 0) / (num_q_heads / num_kv_heads);
   const int ps_mask = (1 << log2_ps) - 1;
-  const size_t token_stride = (size_t)num_kv_heads * D;  // elements between tokens
+  const int token_bytes = num_kv_heads * D * 2;  // bytes between tokens in the pools
+  // this lane's 16 bytes inside a token row; rows of absent heads load nothing
+  const uint32_t lane_off = active ? (uint32_t)((hk * D + col * 8) * 2) : kOutside;
 
   // query slice of this lane, pre-multiplied by scale * log2(e)
   float qf[8];
@@ -104,35 +115,49 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   int chunk_page = 0;
   if (lane < n_chunks)
     chunk_page = block_table[(size_t)b * max_pages + ((t_begin + lane * kChunk) >> log2_ps)];
+  // these loads complete here: the ring's loads below are not tracked by the compiler,
+  // so no wait it would place for these may be left to count them
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // Step s = chunk s: this wave's tokens t_begin + 16 s + 4 w .. + 3 go to ring slot
+  // s % kRing.  Steps past the end are issued too, with every lane out of range (they
+  // write zeros to a free slot and read nothing), so each step is 8 loads and the
+  // waits below are constants.
+  const uint32_t ring_base = lds_address(ring) + (uint32_t)(wave * kRing * kSlotBytes);
+  auto issue = [&](int s) {
+    const int t0 = t_begin + s * kChunk + wave * kStep;
+    const uint32_t slot = ring_base + (uint32_t)((s % kRing) * kSlotBytes);
+    const bool live = s < n_chunks;
+    const int phys = live ? __builtin_amdgcn_readlane(chunk_page, min(s, 63)) : 0;
+    const size_t row0 = (((size_t)phys << log2_ps) + (t0 & ps_mask)) * (size_t)token_bytes;
+    const u32x4 rk = buffer_words(reinterpret_cast<const char*>(k_pool) + row0, kAllBytes);
+    const u32x4 rv = buffer_words(reinterpret_cast<const char*>(v_pool) + row0, kAllBytes);
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+      const bool ok = live && t0 + i < t_end && t0 + i >= t_lo;
+      const int voff = (int)(ok ? lane_off + (uint32_t)(i * token_bytes) : kOutside);
+      lds_load16(rk, slot + i * 1024, voff);
+      lds_load16(rv, slot + (kStep + i) * 1024, voff);
+    }
+  };
 
   float m = kEmptyMax, l = 0.f;
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
 
-  // loads of this wave's tokens of chunk c
-  auto issue = [&](int c, u32x4* kd, u32x4* vd) {
-    const int t0 = t_begin + c * kChunk + wave * kTokPerWave;
-    const int phys = __builtin_amdgcn_readlane(chunk_page, c);
-    const size_t base = (((size_t)phys << log2_ps) + (t0 & ps_mask)) * token_stride +
-                        (size_t)hk * D + col * 8;
+  auto consume = [&](int s) {
+    const int t0 = t_begin + s * kChunk + wave * kStep;
+    const char* src = ring + wave * kRing * kSlotBytes + (s % kRing) * kSlotBytes + lane * 16;
+    u32x4 kc[kStep], vc[kStep];
 #pragma unroll
-    for (int i = 0; i < kTokPerWave; ++i) {
-      if (active && t0 + i < t_end && t0 + i >= t_lo) {
-        kd[i] = *reinterpret_cast<const u32x4*>(k_pool + base + i * token_stride);
-        vd[i] = *reinterpret_cast<const u32x4*>(v_pool + base + i * token_stride);
-      } else {
-        kd[i] = u32x4{0u, 0u, 0u, 0u};
-        vd[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < kStep; ++i) {
+      kc[i] = *reinterpret_cast<const u32x4*>(src + i * 1024);
+      vc[i] = *reinterpret_cast<const u32x4*>(src + (kStep + i) * 1024);
     }
-  };
-
-  auto consume = [&](int c, const u32x4* kc, const u32x4* vc) {
-    const int t0 = t_begin + c * kChunk + wave * kTokPerWave;
-    float s[kTokPerWave];
+    float sc[kStep];
 #pragma unroll
-    for (int i = 0; i < kTokPerWave; ++i) {
+    for (int i = 0; i < kStep; ++i) {
       float acc = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -140,18 +165,18 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         acc = fmaf(qf[2 * w + 1], bf16_hi(kc[i][w]), acc);
       }
       acc = group_sum<G::kLanesPerHead>(acc);
-      s[i] = (t0 + i < t_end && t0 + i >= t_lo) ? acc : -INFINITY;
+      sc[i] = (t0 + i < t_end && t0 + i >= t_lo) ? acc : -INFINITY;
     }
-    float mx = s[0];
+    float mx = sc[0];
 #pragma unroll
-    for (int i = 1; i < kTokPerWave; ++i) mx = fmaxf(mx, s[i]);
+    for (int i = 1; i < kStep; ++i) mx = fmaxf(mx, sc[i]);
     const float m_new = fmaxf(m, mx);
     const float alpha = fast_exp2(m - m_new);
     float psum = 0.f;
-    float p[kTokPerWave];
+    float p[kStep];
 #pragma unroll
-    for (int i = 0; i < kTokPerWave; ++i) {
-      p[i] = fast_exp2(s[i] - m_new);
+    for (int i = 0; i < kStep; ++i) {
+      p[i] = fast_exp2(sc[i] - m_new);
       psum += p[i];
     }
     l = l * alpha + psum;
@@ -160,7 +185,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       float lo = o[2 * w] * alpha;
       float hi = o[2 * w + 1] * alpha;
 #pragma unroll
-      for (int i = 0; i < kTokPerWave; ++i) {
+      for (int i = 0; i < kStep; ++i) {
         lo = fmaf(p[i], bf16_lo(vc[i][w]), lo);
         hi = fmaf(p[i], bf16_hi(vc[i][w]), hi);
       }
@@ -170,23 +195,22 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     m = m_new;
   };
 
-  // three register buffers: chunk c is consumed while c+1 and c+2 are in flight
-  u32x4 ka[kTokPerWave], va[kTokPerWave], kb[kTokPerWave], vb[kTokPerWave];
-  u32x4 kc[kTokPerWave], vc[kTokPerWave];
-  issue(0, ka, va);
-  if (n_chunks > 1) issue(1, kb, vb);
-  for (int c = 0; c < n_chunks; c += 3) {
-    if (c + 2 < n_chunks) issue(c + 2, kc, vc);
-    consume(c, ka, va);
-    if (c + 1 >= n_chunks) break;
-    if (c + 3 < n_chunks) issue(c + 3, ka, va);
-    consume(c + 1, kb, vb);
-    if (c + 2 >= n_chunks) break;
-    if (c + 4 < n_chunks) issue(c + 4, kb, vb);
-    consume(c + 2, kc, vc);
+#pragma unroll
+  for (int s = 0; s < kRing - 1; ++s) issue(s);
+  for (int s = 0; s < n_chunks; ++s) {
+    // slot (s - 1) % kRing was read back by the previous consume, whose arithmetic
+    // waited for those LDS reads, so it can take step s + kRing - 1 now
+    issue(s + kRing - 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kRing - 1) * 2 * kStep));  // step s landed
+    consume(s);
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();  // every wave is done with the ring, which now holds the merge arrays
 
   // merge the 4 waves' states per head and write the split's partial
+  auto sm_o = reinterpret_cast<float (*)[G::kHeads][D]>(ring);
+  auto sm_m = reinterpret_cast<float (*)[G::kHeads]>(ring + kWaves * G::kHeads * D * 4);
+  auto sm_l = reinterpret_cast<float (*)[G::kHeads]>(ring + kWaves * G::kHeads * (D + 1) * 4);
 #pragma unroll
   for (int i = 0; i < 8; ++i) sm_o[wave][row][col * 8 + i] = o[i];
   if (col == 0) {

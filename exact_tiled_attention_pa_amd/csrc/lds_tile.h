@@ -19,6 +19,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
 }
 
+// Raw buffer resource words over [base, base + bytes), for loads written in inline
+// assembly.  User-space addresses are below 2^47, so the stride field stays zero.
+__device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferFlags};
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from byte offset voffset of the buffer
+// into LDS at lds_addr + 16 * lane; lanes whose offset lies outside the buffer write
+// zeros and read nothing.  Written as inline assembly so the compiler does not track
+// it (it would otherwise wait for these loads before unrelated LDS reads): callers
+// wait with explicit vmcnt waits, and must have no compiler-visible vector memory
+// loads of their own in flight while these are outstanding.
+__device__ __forceinline__ void lds_load16(u32x4 rsrc, uint32_t lds_addr, int voffset) {
+  __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       ::"s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory");
+}
+
+// LDS byte address of a __shared__ object, as M0 takes it.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// s_waitcnt immediate for vmcnt(n) (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // XOR swizzles of the 16-byte chunks of an LDS row r holding D bf16 values.
 //   K: chunk c of row r sits in slot c ^ (r mod chunks): the ds_read_b128 of 32
 //      consecutive rows at one chunk hit distinct banks.

@@ -103,11 +103,44 @@ def recorded_traffic(kind: str, workload: str):
         return None
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_CYCLES")
+
+
+def mfma_busy_fraction(mfma_busy_cycles, sq_cycles, simd_count, shader_engines):
+    """Share of the kernel's duration the matrix cores were busy: SQ_VALU_MFMA_BUSY_CYCLES
+    is summed over every SIMD and SQ_CYCLES over every shader engine's sequencer, so the
+    kernel's duration in shader cycles is SQ_CYCLES / shader_engines."""
+    return mfma_busy_cycles / (simd_count * sq_cycles / shader_engines)
+
+
+def recorded_mfma(kind: str, workload: str):
+    """Matrix-core busy fraction from the committed counter summary, or None if absent
+    or if the kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{KERNEL_FILES[kind]}.{workload}.mfma.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_digest(kind):
+        return None
+    try:
+        return float(vals["mfma_busy_fraction"])
+    except (KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------------ GPU legs
+
+GQA_MIN_GROUP = 4  # query heads per K/V head from which the library runs decode_gqa_kernel
+
 
 def decode_kind(wl) -> str:
     """Which pass-1 decode kernel the library runs for this head layout."""
-    return "decode_gqa" if wl.num_q_heads // wl.heads >= 2 else "decode"
+    return "decode_gqa" if wl.num_q_heads // wl.heads >= GQA_MIN_GROUP else "decode"
 
 
 def decode_kernel_name(wl) -> str:
@@ -283,6 +316,7 @@ def prefill_summary(wl, call, steps, warmup):
     avg = sum(ms) / len(ms)
     tflops = flops / (avg * 1e-3) / 1e12
     traffic = recorded_traffic("prefill", wl.name)
+    mfma_busy = recorded_mfma("prefill", wl.name) if call.causal else None
     return {
         "workload": wl.name,
         "tflops": round(tflops, 2),
@@ -292,7 +326,8 @@ def prefill_summary(wl, call, steps, warmup):
         "flops_per_launch": flops,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "mfma_busy": mfma_busy},
         "alg_bytes_per_launch": nbytes,
     }
 
@@ -455,6 +490,42 @@ def summarize_traffic(fetch_dir, write_dir, kind, workload, out_path, command):
     print("\n".join(lines))
 
 
+def summarize_mfma(pmc_dir, kind, workload, out_path, command):
+    """Matrix-core busy fraction of one kernel from a --pmc run of MFMA_COUNTERS,
+    averaged over its dispatches, with the GPU's SIMD and shader-engine counts taken
+    from the same run's agent table."""
+    tag = KERNEL_TAGS[kind]
+    per = {}
+    for r in _read_csv(os.path.join(pmc_dir, "run_counter_collection.csv")):
+        if tag in r["Kernel_Name"] and r["Counter_Name"] in MFMA_COUNTERS:
+            per.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    per = {k: v for k, v in per.items() if len(v) == len(MFMA_COUNTERS)}
+    gpus = [a for a in _read_csv(os.path.join(pmc_dir, "run_agent_info.csv"))
+            if a.get("Agent_Type", "").strip('"') == "GPU"]
+    if not per or not gpus:
+        raise SystemExit(f"no {tag} dispatch with {MFMA_COUNTERS} or no GPU agent in {pmc_dir}")
+    simds, engines = int(gpus[0]["Simd_Count"]), int(gpus[0]["Num_Shader_Banks"])
+    fr = [mfma_busy_fraction(v["SQ_VALU_MFMA_BUSY_CYCLES"], v["SQ_CYCLES"], simds, engines)
+          for v in per.values()]
+    cyc = [v["SQ_CYCLES"] / engines for v in per.values()]
+    src = kind if kind in KERNEL_SOURCES else "prefill"
+    lines = [f"# matrix-core busy fraction of {tag} on workload {workload}",
+             f"# command: {command}",
+             "# fraction = SQ_VALU_MFMA_BUSY_CYCLES / (simd_count * SQ_CYCLES / shader_engines),",
+             "# averaged over dispatches; bench.py reports it only while source_sha256 matches",
+             f"kernel={tag}",
+             f"workload={workload}",
+             f"dispatches={len(fr)}",
+             f"simd_count={simds}",
+             f"shader_engines={engines}",
+             f"shader_cycles_per_launch={sum(cyc) / len(cyc):.0f}",
+             f"mfma_busy_fraction={sum(fr) / len(fr):.4f}",
+             f"source_sha256={source_digest(src)}"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -480,6 +551,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=5,
                     metavar=("FETCH_DIR", "WRITE_DIR", "KIND", "WORKLOAD", "OUT"),
                     help="write the calibrated HBM traffic of one kernel and exit")
+    ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC_DIR", "KIND", "WORKLOAD", "OUT"),
+                    help="write the matrix-core busy fraction of one kernel and exit")
     ap.add_argument("--profile-command", default="",
                     help="the command recorded in a summary")
     args = ap.parse_args()
@@ -488,6 +561,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.profile_command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.profile_command)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

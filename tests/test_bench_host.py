@@ -20,3 +20,51 @@ def test_causal_full_prefill_pairs_closed_form():
     assert bench.visible_pairs([N], [N], True) == N * (N + 1) // 2
     # 4*d*H*pairs for the causal N=4096, 32-head, d=128 prefill: 137.5 GFLOP
     assert abs(4 * 128 * 32 * bench.visible_pairs([N], [N], True) - 137.5e9) < 0.1e9
+
+
+def test_mfma_busy_fraction_from_a_counter_run(tmp_path):
+    """Two dispatches of the causal prefill kernel plus an unrelated kernel: the summary
+    averages the per-dispatch fractions of the prefill kernel only."""
+    import csv
+
+    head = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    # shader cycles per launch = SQ_CYCLES / 32 engines; busy cycles summed over 1024 SIMDs
+    for disp, (busy, sq) in {"7": (0.5 * 1024 * 300000, 32 * 300000),
+                             "9": (0.25 * 1024 * 200000, 32 * 200000)}.items():
+        rows.append([disp, "pa::prefill_kernel<128, true>", "SQ_VALU_MFMA_BUSY_CYCLES", busy])
+        rows.append([disp, "pa::prefill_kernel<128, true>", "SQ_CYCLES", sq])
+    rows.append(["8", "pa::decode_partial_kernel<128>", "SQ_VALU_MFMA_BUSY_CYCLES", 1.0])
+    rows.append(["8", "pa::decode_partial_kernel<128>", "SQ_CYCLES", 1.0])
+    with open(tmp_path / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(head)
+        w.writerows(rows)
+    with open(tmp_path / "run_agent_info.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Agent_Type", "Simd_Count", "Num_Shader_Banks"])
+        w.writerow(["CPU", "0", "0"])
+        w.writerow(["GPU", "1024", "32"])
+    out = tmp_path / "summary.txt"
+    bench.summarize_mfma(str(tmp_path), "prefill", "prefill_4096_causal", str(out), "cmd")
+    vals = dict(l.split("=", 1) for l in out.read_text().splitlines() if "=" in l
+                and not l.startswith("#"))
+    assert vals["dispatches"] == "2"
+    assert abs(float(vals["mfma_busy_fraction"]) - 0.375) < 1e-9
+    assert vals["source_sha256"] == bench.source_digest("prefill")
+
+
+def test_decode_kind_follows_the_library_dispatch():
+    class Wl:
+        def __init__(self, hq, hkv):
+            self.num_q_heads, self.heads = hq, hkv
+    assert bench.decode_kind(Wl(32, 32)) == "decode"
+    assert bench.decode_kind(Wl(32, 16)) == "decode"    # g = 2: one-head-per-row kernel
+    assert bench.decode_kind(Wl(24, 8)) == "decode"     # g = 3
+    assert bench.decode_kind(Wl(32, 8)) == "decode_gqa"
+
+
+def test_gqa_threshold_matches_the_library():
+    import re
+    text = open(bench.os.path.join(bench.CSRC, "kernels.h")).read()
+    assert int(re.search(r"kGqaMinGroup\s*=\s*(\d+)", text).group(1)) == bench.GQA_MIN_GROUP

@@ -97,6 +97,11 @@ DECODE_CASES = [
     (64, 64, 71, 1, [65, 1, 2000]),       # 71 heads: blocks of 32 + 32 + 7
     (128, 256, 16, 2, [1, 255, 256, 257, 1023, 1024, 1025, 5000]),
     (64, 128, 8, 1, [127, 128, 129, 2049]),
+    # one-head-per-row kernel: a last head group with absent heads, splits shorter than
+    # its load ring, and 3 query heads per K/V head
+    (128, 16, 5, 5, [1, 16, 63, 64, 65, 300]),
+    (128, 16, 6, 2, [17, 1000]),
+    (64, 32, 9, 3, [33, 2049]),
 ]
 
 

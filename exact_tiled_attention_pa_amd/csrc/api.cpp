@@ -104,6 +104,8 @@ size_t ws_ml_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layou
   return (n * sizeof(float) + 255) / 256 * 256;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
                         const int32_t* block_table, const int32_t* seq_lens, float scale,
                         int32_t batch, int32_t num_q_heads, const void* workspace,
@@ -115,6 +117,8 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
   if (need_inputs) {
     if (!q || !k_pool || !v_pool || !block_table)
       return fail(PA_ERR_NULL, "q, k_pool, v_pool and block_table must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+      return fail(PA_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
     st = check_scale(scale);
     if (st) return st;
   }
@@ -124,6 +128,8 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
                 "decode splits", (long long)layout->max_pages_per_seq * layout->page_size);
   const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned16(workspace))
+    return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is too small (need %zu)",
                 workspace_bytes, need);
@@ -157,8 +163,6 @@ pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf1
   a.window = window;
   return a;
 }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
@@ -196,6 +200,8 @@ int pa_prefill_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_
   if (st) return st;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out || !q_start)
     return fail(PA_ERR_NULL, "every array argument of pa_prefill must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(PA_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
   if (batch == 0 || max_q_len == 0) return ok();
 
   pa::PrefillArgs a;

@@ -107,8 +107,9 @@ typedef struct pa_kv_layout {
  *                h / (num_q_heads / num_kv_heads)
  *   max_q_len    host-side upper bound of every q_len_b (sizes the grid without
  *                reading device memory); rows past q_len_b are never written
+ * q, k_pool, v_pool and out must be 16-byte aligned (the kernels move 16-byte pieces).
  * Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG (sizes, scale, max_q_len above
- * max_pages_per_seq * page_size), PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ * max_pages_per_seq * page_size, misaligned arrays), PA_ERR_UNSUPPORTED, PA_ERR_HIP.
  */
 int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
                const int32_t* block_table, const int32_t* seq_lens, int causal,
@@ -142,10 +143,11 @@ int32_t pa_decode_split_tokens(int32_t num_q_heads, const pa_kv_layout* layout);
  *   scale     finite and >= 0
  *   out       [batch, num_q_heads, head_dim] bf16
  *   workspace device buffer of at least pa_decode_workspace_bytes(...) bytes,
- *             any contents; calls that share a workspace must be ordered on
- *             one stream
- * Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
- * PA_ERR_HIP.
+ *             16-byte aligned, any contents; calls that share a workspace must be
+ *             ordered on one stream
+ * q, k_pool and v_pool must be 16-byte aligned (the kernels move 16-byte pieces).
+ * Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG (sizes, scale, misaligned arrays),
+ * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE (missing, too small or misaligned), PA_ERR_HIP.
  */
 int pa_decode(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
               const int32_t* block_table, const int32_t* seq_lens, float scale,

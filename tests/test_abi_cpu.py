@@ -66,6 +66,9 @@ def prefill(lib, layout, *, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, causal=1
     (dict(scale=float("inf")), {}, B.PA_ERR_INVALID_ARG),
     (dict(max_q_len=769), {}, B.PA_ERR_INVALID_ARG),   # 3 pages of 256 hold 768 tokens
     (dict(max_q_len=-5), {}, B.PA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), {}, B.PA_ERR_INVALID_ARG),      # 16-byte pieces: aligned arrays
+    (dict(k=FAKE + 8), {}, B.PA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), {}, B.PA_ERR_INVALID_ARG),
 ])
 def test_prefill_rejects(lib, kw, layout_kw, status):
     st = prefill(lib, lay(**layout_kw), **kw)
@@ -133,6 +136,9 @@ def test_decode_rejects(lib):
     assert call(scale=float("nan")) == B.PA_ERR_INVALID_ARG
     assert call(hq=6) == B.PA_ERR_INVALID_ARG
     assert call(layout=B.make_layout(100, 16, 4, 80, 10)) == B.PA_ERR_UNSUPPORTED
+    assert call(q=FAKE + 2) == B.PA_ERR_INVALID_ARG
+    assert call(ws=FAKE + 4) == B.PA_ERR_WORKSPACE
+    assert "aligned" in B.last_error()
     assert call(batch=0) == B.PA_OK
     st = lib.pa_decode_partial(FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 2, 4, None, need,
                                ctypes.byref(layout), None)

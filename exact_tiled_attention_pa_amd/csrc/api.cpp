@@ -68,6 +68,10 @@ int check_layout(const pa_kv_layout* layout, int32_t num_q_heads) {
     return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size exceeds 2^30 tokens");
   if ((int64_t)layout->num_pages * layout->page_size > ((int64_t)1 << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "num_pages * page_size exceeds 2^31 - 1 token rows");
+  // a token row of the pools at most 32 MiB: the kernels' in-page byte offsets (16 rows
+  // at most) then stay below 2^31
+  if ((int64_t)layout->num_kv_heads * layout->head_dim > (int64_t)1 << 24)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads * head_dim exceeds 2^24");
   return PA_OK;
 }
 
@@ -305,8 +309,6 @@ int pa_kv_append(const pa_bf16* k_new, const pa_bf16* v_new, const int32_t* seq_
   if (st) return st;
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens=%d must be >= 0", num_tokens);
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d must be >= 0", num_seqs);
-  if ((int64_t)layout->num_kv_heads * layout->head_dim > (int64_t)1 << 24)
-    return fail(PA_ERR_INVALID_ARG, "num_kv_heads * head_dim exceeds 2^24");
   if (!k_new || !v_new || !seq_ids || !positions || !k_pool || !v_pool || !block_table)
     return fail(PA_ERR_NULL, "every array argument of pa_kv_append must be non-NULL");
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))

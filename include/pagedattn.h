@@ -80,7 +80,8 @@ typedef struct pa_kv_layout {
   int32_t num_pages;          /* physical pages in each pool, >= 1;
                                  num_pages * page_size < 2^31 */
   int32_t page_size;          /* tokens per page: a power of two in [16, 256] */
-  int32_t num_kv_heads;       /* heads stored per token in the pools, >= 1 */
+  int32_t num_kv_heads;       /* heads stored per token in the pools, >= 1;
+                                 num_kv_heads * head_dim <= 2^24 */
   int32_t head_dim;           /* 64 or 128 */
   int32_t max_pages_per_seq;  /* row length (int32 elements) of block_table, >= 1 */
 } pa_kv_layout;

@@ -91,6 +91,16 @@ def test_window_argument_errors(lib):
     assert st == B.PA_ERR_INVALID_ARG
 
 
+def test_token_rows_above_32_mib_are_rejected(lib):
+    layout = lay(hkv=131073, d=128)
+    assert prefill(lib, layout, hq=131073) == B.PA_ERR_INVALID_ARG
+    assert "2^24" in B.last_error()
+    # exactly 2^24 elements per token row is accepted
+    ok = lay(hkv=131072, d=128)
+    assert lib.pa_decode_split_tokens(131072, ctypes.byref(ok)) == 256
+    assert lib.pa_decode_split_tokens(131073, ctypes.byref(layout)) == 0
+
+
 def test_prefill_empty_batch_is_ok_without_device(lib):
     assert prefill(lib, lay(), batch=0) == B.PA_OK
     assert prefill(lib, lay(), max_q_len=0) == B.PA_OK

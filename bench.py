@@ -640,9 +640,6 @@ def main():
             t_meas = (split_avg + sum(comb_ms) / len(comb_ms) + cs["kernel_ms_avg"]) * 1e-3
             result["chunks"] = cs
             result["combined_roofline_fraction"] = round(t_roof / t_meas, 4)
-        if not args.no_next and len(wl.calls) == 1 and wl.name == "decode_64":
-            log("rows beyond the core path: grouped heads, append, page copy, windows")
-            result["next_rows"] = next_rows_summary(wl, args.steps, args.warmup)
     else:
         s = prefill_summary(wl, call, args.steps, args.warmup)
         result.update({
@@ -667,6 +664,12 @@ def main():
                                                      max(args.warmup, 3))
             del pw
             torch.cuda.empty_cache()
+
+    # the rows beyond the core path run after the headline legs
+    if (not args.no_next and call.kind == "decode" and len(wl.calls) == 1
+            and wl.name == "decode_64"):
+        log("rows beyond the core path: grouped heads, append, page copy, windows")
+        result["next_rows"] = next_rows_summary(wl, args.steps, args.warmup)
 
     # the oracle runs last, after every GPU leg, so its host time cannot idle the GPU
     # between a warm-up and a timed region

@@ -74,9 +74,10 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __shared__ __attribute__((aligned(1024))) char ring[kRingBytes];
 
   const int hg = blockIdx.x;
-  const int split = blockIdx.y;
   const int b = blockIdx.z;
   const int seq_len = seq_lens[b];
+  const int split = decode_split_of(blockIdx.y, seq_len, split_tokens, window);
+  if (split < 0) return;
   const int t_begin = split * split_tokens;
   if (t_begin >= seq_len) return;  // the combine pass never reads this split
   const int t_end = min(seq_len, t_begin + split_tokens);
@@ -306,7 +307,7 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
 template <int D>
 void launch_partial(const DecodeArgs& a, hipStream_t stream) {
   using G = DecodeGeometry<D>;
-  const dim3 grid((a.num_q_heads + G::kHeads - 1) / G::kHeads, a.max_splits, a.batch);
+  const dim3 grid((a.num_q_heads + G::kHeads - 1) / G::kHeads, decode_grid_splits(a), a.batch);
   hipLaunchKernelGGL(decode_partial_kernel<D>, grid, dim3(kThreads), 0, stream, a.q, a.k_pool,
                      a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
                      score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,

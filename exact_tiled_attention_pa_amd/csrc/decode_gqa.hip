@@ -80,9 +80,10 @@ decode_gqa_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int hb = blockIdx.x % blocks_per_kv;
   const int h0 = hk * group + hb * kHeadBlock;          // first query head of the block
   const int nh = min(kHeadBlock, group - hb * kHeadBlock);
-  const int split = blockIdx.y;
   const int b = blockIdx.z;
   const int seq_len = seq_lens[b];
+  const int split = decode_split_of(blockIdx.y, seq_len, split_tokens, window);
+  if (split < 0) return;
   const int t_begin = split * split_tokens;
   if (t_begin >= seq_len) return;  // the combine pass never reads this split
   const int t_end = min(seq_len, t_begin + split_tokens);
@@ -317,7 +318,7 @@ template <int D>
 void launch_gqa(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int blocks_per_kv = (group + kHeadBlock - 1) / kHeadBlock;
-  const dim3 grid(a.num_kv_heads * blocks_per_kv, a.max_splits, a.batch);
+  const dim3 grid(a.num_kv_heads * blocks_per_kv, decode_grid_splits(a), a.batch);
   hipLaunchKernelGGL(decode_gqa_kernel<D>, grid, dim3(kThreads), 0, stream, a.q, a.k_pool,
                      a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
                      score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,

@@ -73,6 +73,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Split walked by decode grid row y (see decode_grid_splits): with a sliding window the
+// rows count back from the sequence's last split, else row y is split y.  Negative:
+// nothing to do.
+__device__ __forceinline__ int decode_split_of(int y, int seq_len, int split_tokens,
+                                               int window) {
+  return window > 0 ? (seq_len > 0 ? (seq_len - 1) / split_tokens : 0) - y : y;
+}
+
 // Factor applied to raw q.k dot products: scale * log2(e), so that softmax
 // weights are exp2(s * c - m).  A zero scale is raised to the smallest normal
 // float: every finite score then maps to exactly exp2(0) = 1 (uniform weights,

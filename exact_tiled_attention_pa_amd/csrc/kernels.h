@@ -49,6 +49,16 @@ struct DecodeArgs {
   int window;  // sliding-window length (0: none)
 };
 
+// Decode grids: with a sliding window only the splits that can hold keys inside it
+// are launched, counted back from each sequence's last split (a window of w keys
+// touches at most ceil(w / split_tokens) + 1 splits); grid row y then walks split
+// (L_b - 1) / split_tokens - y (decode_split_of).  Without a window row y is split y.
+inline int decode_grid_splits(const DecodeArgs& a) {
+  if (a.window <= 0) return a.max_splits;
+  const int n = (a.window + a.split_tokens - 1) / a.split_tokens + 1;
+  return n < a.max_splits ? n : a.max_splits;
+}
+
 struct KvAppendArgs {
   const uint16_t* k_new;  // [num_tokens, num_kv_heads, head_dim]
   const uint16_t* v_new;

@@ -28,9 +28,8 @@
 //     Memory-Efficient Attention for LLMs", "The Algorithm"), the 4 waves' states
 //     are merged through LDS and the split's (m, l, unnormalised O) goes to the
 //     workspace.
-//   pass 2 (decode_combine_kernel): per (sequence, head), merges the splits'
-//     partials with the same rescaling algebra (4 waves share the splits) and
-//     writes bf16 O.
+//   pass 2 (decode_combine_kernel): one wave per (sequence, head) merges the
+//     splits' partials in order with the same rescaling algebra and writes bf16 O.
 //
 // Query head h reads K/V head h / (num_q_heads / num_kv_heads).  m is kept in
 // log2 units (scores times scale * log2(e)) so every exponential is one v_exp_f32.
@@ -243,9 +242,11 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
 }
 
-// One workgroup per (sequence, head): the global max of the splits' m first, then
-// the 4 waves take every 4th split (lanes cover d), then an LDS sum of the waves.
+// One wave per (sequence, head), four heads per workgroup: the wave walks the splits
+// in order with the same online rescaling as pass 1 (running max, rescaled sum and
+// output), each lane holding D / 64 output columns, and writes O / l as bf16.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineHeads = kCombineThreads / 64;
 
 template <int D>
 __global__ void __launch_bounds__(kCombineThreads)
@@ -253,55 +254,47 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
                       const float* __restrict__ ws_ml, uint16_t* __restrict__ out,
                       int num_q_heads, int split_tokens, int max_splits, int window) {
   constexpr int kPerLane = D / 64;
-  __shared__ float sm_max[kWaves];
-  __shared__ float sm_l[kWaves];
-  __shared__ float sm_acc[kWaves][D];
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x * kCombineHeads + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (h >= num_q_heads) return;
+  const int b = blockIdx.y;
   const int seq_len = seq_lens[b];
   const int n_splits = seq_len > 0 ? (seq_len + split_tokens - 1) / split_tokens : 0;
   const int s_first = window > 0 ? max(0, seq_len - window) / split_tokens : 0;
   const size_t slot0 = ((size_t)b * num_q_heads + h) * max_splits;
 
-  float mx = kEmptyMax;
-  for (int s = s_first + threadIdx.x; s < n_splits; s += kCombineThreads)
-    mx = fmaxf(mx, ws_ml[(slot0 + s) * 2]);
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) sm_max[wave] = mx;
-  __syncthreads();
-  float big = sm_max[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) big = fmaxf(big, sm_max[w]);
-
+  float m = kEmptyMax, l = 0.f;
   float acc[kPerLane];
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e) acc[e] = 0.f;
-  float lsum = 0.f;
-  for (int s = s_first + wave; s < n_splits; s += kWaves) {
-    const float m_s = ws_ml[(slot0 + s) * 2];
-    const float l_s = ws_ml[(slot0 + s) * 2 + 1];
-    const float w = fast_exp2(m_s - big);
-    const float* o_s = ws_o + (slot0 + s) * D + lane * kPerLane;
+  // splits in groups of kGroup: every load of a group is issued before any of its
+  // partials is folded in (absent splits of the last group fold in with weight 0)
+  constexpr int kGroup = 8;
+  for (int s0 = s_first; s0 < n_splits; s0 += kGroup) {
+    float ms[kGroup], ls[kGroup], os[kGroup][kPerLane];
 #pragma unroll
-    for (int e = 0; e < kPerLane; ++e) acc[e] = fmaf(w, o_s[e], acc[e]);
-    lsum = fmaf(w, l_s, lsum);
-  }
+    for (int i = 0; i < kGroup; ++i) {
+      const int s = min(s0 + i, n_splits - 1);
+      ms[i] = s0 + i < n_splits ? ws_ml[(slot0 + s) * 2] : kEmptyMax;
+      ls[i] = ws_ml[(slot0 + s) * 2 + 1];
 #pragma unroll
-  for (int e = 0; e < kPerLane; ++e) sm_acc[wave][lane * kPerLane + e] = acc[e];
-  if (lane == 0) sm_l[wave] = lsum;
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      o += sm_acc[w][threadIdx.x];
-      l += sm_l[w];
+      for (int e = 0; e < kPerLane; ++e) os[i][e] = ws_o[(slot0 + s) * D + lane * kPerLane + e];
     }
-    const float r = l > 0.f ? o / l : 0.f;
-    out[((size_t)b * num_q_heads + h) * D + threadIdx.x] = to_bf16_bits(r);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const float m_new = fmaxf(m, ms[i]);
+      const float a = fast_exp2(m - m_new);
+      const float w = fast_exp2(ms[i] - m_new);
+      l = fmaf(l, a, w * ls[i]);
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) acc[e] = fmaf(acc[e], a, w * os[i][e]);
+      m = m_new;
+    }
   }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* dst = out + ((size_t)b * num_q_heads + h) * D + lane * kPerLane;
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) dst[e] = to_bf16_bits(acc[e] * inv);
 }
 
 template <int D>
@@ -325,7 +318,7 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_q_heads, a.batch);
+  const dim3 grid((a.num_q_heads + kCombineHeads - 1) / kCombineHeads, a.batch);
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(kCombineThreads), 0, stream,
                        a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,

@@ -31,7 +31,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_pa_amd", "csrc")
 KERNEL_SOURCES = {
-    "decode": ["decode.hip", "device_util.h", "kernels.h"],
+    "decode": ["decode.hip", "device_util.h", "lds_tile.h", "kernels.h"],
     "decode_gqa": ["decode_gqa.hip", "device_util.h", "lds_tile.h", "kernels.h"],
     "prefill": ["prefill.hip", "device_util.h", "lds_tile.h", "kernels.h"],
 }

@@ -68,3 +68,13 @@ def test_gqa_threshold_matches_the_library():
     import re
     text = open(bench.os.path.join(bench.CSRC, "kernels.h")).read()
     assert int(re.search(r"kGqaMinGroup\s*=\s*(\d+)", text).group(1)) == bench.GQA_MIN_GROUP
+
+
+def test_kernel_source_lists_cover_local_includes():
+    """The source hash that guards each counter summary covers every local header the
+    kernel's file includes."""
+    import re
+    for kind, files in bench.KERNEL_SOURCES.items():
+        text = open(bench.os.path.join(bench.CSRC, files[0])).read()
+        for inc in re.findall(r'#include "([^"]+)"', text):
+            assert inc in files, (kind, inc)

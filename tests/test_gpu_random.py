@@ -104,3 +104,30 @@ def test_random_prefill(seed):
     ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, causal,
                               wl.scale, window=window)
     G.compare(G.bf16_out_to_f64(out), ref, f"random prefill seed={seed}")
+
+
+def test_many_short_sequences_decode_and_prefill():
+    """Thousands of short decode sequences (grid z in the thousands, one chunk per
+    split) and hundreds of short prefill chunks in one call."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 80, size=3000)]
+    G.banner(f"many sequences: decode batch={len(lens)}")
+    wl = W.build("many_dec", 78, heads=2, head_dim=64, page_size=16, lens=lens, kind="decode",
+                 pool_slack=1.1, device="cuda", poison=True, q_heads=4)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
+    k, v = _repeat_heads(k, v, 2)
+    ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale)
+    G.compare(G.bf16_out_to_f64(out), ref, "many short decode sequences")
+
+    lens = [int(x) for x in rng.integers(1, 300, size=300)]
+    q_lens = [int(rng.integers(0, min(L, 40) + 1)) for L in lens]
+    G.banner(f"many sequences: prefill batch={len(lens)} rows={sum(q_lens)}")
+    wl = W.build("many_pre", 79, heads=2, head_dim=128, page_size=32, lens=lens, q_lens=q_lens,
+                 causal=True, pool_slack=1.1, device="cuda", poison=True)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), "many short prefill chunks")

@@ -95,8 +95,12 @@ def compare(got: np.ndarray, ref: np.ndarray, what: str, max_tol=MAX_ABS_TOL,
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
     err = np.abs(g - r)
     rms = float(np.sqrt(np.mean(r * r)))
+    # the worst element against half a bf16 ulp of its reference value: the rounding
+    # of the output itself, which no kernel can avoid
+    w = int(np.argmax(err))
+    half_ulp = 2.0 ** (np.floor(np.log2(max(abs(float(r[w])), 2.0 ** -126))) - 8)
     print(f"[parity] {what}: n={err.size} max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
-          f"rms_ref={rms:.3e}", flush=True)
+          f"rms_ref={rms:.3e} worst_ref={float(r[w]):.4f} half_ulp={half_ulp:.2e}", flush=True)
     assert err.max() <= max_tol, f"{what}: max abs error {err.max():.3e} > {max_tol}"
     assert err.mean() <= mean_tol, f"{what}: mean abs error {err.mean():.3e} > {mean_tol}"
     return float(err.max()), float(err.mean())

@@ -78,3 +78,46 @@ def test_kernel_source_lists_cover_local_includes():
         text = open(bench.os.path.join(bench.CSRC, files[0])).read()
         for inc in re.findall(r'#include "([^"]+)"', text):
             assert inc in files, (kind, inc)
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    """FETCH_SIZE and WRITE_SIZE runs, each with a 1 GiB calibration copy: the kernel's
+    readings are scaled by 1 GiB / the copy's reading; bench reads the figure back only
+    while the recorded source hash matches."""
+    import csv
+
+    def run_dir(name, counter, copy_kib, kernel_kib):
+        d = tmp_path / name
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                        "Counter_Value"])
+            w.writerow(["1", "__amd_rocclr_copyBuffer", "1048576", counter, copy_kib])
+            w.writerow(["2", "__amd_rocclr_copyBuffer", "64", counter, 1.0])  # small copy
+            for i, v in enumerate(kernel_kib):
+                w.writerow([str(3 + i), "pa::prefill_kernel<128, true>", "262144", counter, v])
+            w.writerow(["9", "pa::decode_partial_kernel<128>", "262144", counter, 1e9])
+        return str(d)
+
+    gib_kib = float(1 << 20)
+    fetch = run_dir("fetch", "FETCH_SIZE", gib_kib / 2, [1000.0, 3000.0])  # factor 2
+    write = run_dir("write", "WRITE_SIZE", gib_kib, [500.0, 500.0])        # factor 1
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    out = tmp_path / f"{bench.KERNEL_FILES['prefill']}.wl.traffic.txt"
+    bench.summarize_traffic(fetch, write, "prefill", "wl", str(out), "cmd")
+    expect = (2000.0 * 2 + 500.0 * 1) * 1024
+    assert bench.recorded_traffic("prefill", "wl") == int(expect)
+    # a summary taken from other kernel sources is not reported
+    text = out.read_text().replace(bench.source_digest("prefill"), "0" * 64)
+    out.write_text(text)
+    assert bench.recorded_traffic("prefill", "wl") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=bench.os.path.dirname(
+        bench.os.path.abspath(bench.__file__)), capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

@@ -48,7 +48,8 @@
 //   - P rounded to bf16 feeds O^T += V^T P^T, again 32x32x16 MFMA with fp32
 //     accumulators; V^T fragments come from the transposing LDS read, whose
 //     4-key x 16-d block per 16 lanes matches the MFMA operand layout, with the
-//     key order of the S^T accumulator registers.
+//     key order of the S^T accumulator registers.  All of a tile's V^T fragments
+//     are read at the start of the tile, so those reads overlap S and the softmax.
 // Epilogue: O / l, rounded to bf16 (RNE), staged through LDS and written with
 // 16-byte coalesced stores.
 
@@ -211,6 +212,24 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
 
   auto compute_tile = [&](int j, const char* k_src, const char* v_src) {
     const int kt0 = j * BN;
+    // V^T fragments of the whole tile (64 VGPRs), read before the score MFMAs so that the
+    // transposing LDS reads complete during S and the softmax instead of stalling P V
+    bf16x8 vfr[4][G::kDB];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int db = 0; db < G::kDB; ++db) {
+        const char* base = v_src + c * 16 * G::kRowBytes + v_rd[db];
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * G::kRowBytes));
+        // keep the whole-vector bit casts: element-wise access to these results is not
+        // reliable with this compiler
+        const u32x2 wl = __builtin_bit_cast(u32x2, lo);
+        const u32x2 wh = __builtin_bit_cast(u32x2, hi);
+        vfr[c][db] = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wh[0], wh[1]});
+      }
+
     // S^T (keys x queries) = K Q^T: two 32-key blocks
     f32x16 sacc[2];
 #pragma unroll
@@ -292,16 +311,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int db = 0; db < G::kDB; ++db) {
-        const char* base = v_src + c * 16 * G::kRowBytes + v_rd[db];
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
-        const bf16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * G::kRowBytes));
-        // keep the whole-vector bit casts: element-wise access to these results is not
-        // reliable with this compiler
-        const u32x2 wl = __builtin_bit_cast(u32x2, lo);
-        const u32x2 wh = __builtin_bit_cast(u32x2, hi);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wh[0], wh[1]});
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[db], 0, 0, 0);
+        oacc[db] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[c][db], pb[c], oacc[db], 0, 0, 0);
       }
     }
   };

@@ -30,7 +30,8 @@
 //     XOR-swizzled by the row index, so the K reads (ds_read_b128) and the
 //     transposing V reads (ds_read_b64_tr_b16) are free of bank conflicts;
 //   - two LDS stages: tile j+1 streams in while tile j is computed; one barrier
-//     per tile.
+//     per tile.  The loads of tile j+1 are issued after tile j's S^T MFMAs, so the
+//     scalar work of the issue runs while those MFMAs execute.
 //
 // Per key tile (per wave, 32 query rows):
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q stays in VGPRs for the whole
@@ -210,11 +211,14 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
 
-  auto compute_tile = [&](int j, const char* k_src, const char* v_src) {
-    const int kt0 = j * BN;
+  // A tile is computed in two parts: scores() issues the LDS reads of V^T and K and the
+  // S^T MFMAs, finish_tile() does the masking, the softmax and P V.  The step issues
+  // the next tile's loads in between, so their scalar address work overlaps the MFMAs.
+  f32x16 sacc[2];
+  bf16x8 vfr[4][G::kDB];
+  auto scores = [&](int j, const char* k_src, const char* v_src) {
     // V^T fragments of the whole tile (64 VGPRs), read before the score MFMAs so that the
     // transposing LDS reads complete during S and the softmax instead of stalling P V
-    bf16x8 vfr[4][G::kDB];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -231,7 +235,6 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
       }
 
     // S^T (keys x queries) = K Q^T: two 32-key blocks
-    f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -244,6 +247,9 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
       }
     }
 
+  };
+  auto finish_tile = [&](int j) {
+    const int kt0 = j * BN;
     // mask: register r of block kb holds key kt0 + 32kb + 8(r/4) + 4*half + r%4
     if (j >= full_tiles || j < window_masked_tiles) {
       const int lim = CAUSAL ? min(my_pos, seq_len - 1) : seq_len - 1;
@@ -320,10 +326,12 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
   auto step = [&](int j, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j landed
     __syncthreads();                     // everyone's loads landed; tile j-1 fully consumed
+    // a tile wholly in this wave's causal future, or wholly before its window, is skipped
+    const bool skip = CAUSAL && (j * BN > wave_last_pos || j * BN + BN - 1 < wave_lo);
+    if (!skip) scores(j, k_cur, v_cur);
     if (j + 1 < n_tiles) issue_tile(j + 1, k_nxt, v_nxt);
-    if (CAUSAL && j * BN > wave_last_pos) return;        // whole tile in this wave's future
-    if (CAUSAL && j * BN + BN - 1 < wave_lo) return;     // whole tile before its window
-    compute_tile(j, k_cur, v_cur);
+    if (skip) return;
+    finish_tile(j);
   };
 
   if (first_tile < n_tiles) issue_tile(first_tile, k_lds0, v_lds0);

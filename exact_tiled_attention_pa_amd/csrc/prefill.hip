@@ -234,19 +234,20 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
         vfr[c][db] = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wh[0], wh[1]});
       }
 
-    // S^T (keys x queries) = K Q^T: two 32-key blocks
+    // S^T (keys x queries) = K Q^T: two 32-key blocks whose MFMA chains alternate, so
+    // each pair of K reads feeds two independent MFMAs
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < G::kDK; ++jj) {
+    for (int jj = 0; jj < G::kDK; ++jj)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(k_src + kb * 32 * G::kRowBytes + k_rd[jj]));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[jj], sacc[kb], 0, 0, 0);
       }
-    }
-
   };
   auto finish_tile = [&](int j) {
     const int kt0 = j * BN;

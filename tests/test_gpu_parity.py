@@ -181,6 +181,26 @@ def test_prefill_4096_sampled(causal):
               f"prefill_4096 causal={causal}")
 
 
+def test_prefill_4096_grouped_heads_sampled():
+    """64 query heads over 8 K/V heads at N=4096, causal, shuffled pages of 256: the
+    grouped-head prefill at full size, rows sampled, all query heads checked."""
+    from oracle import attention as OA
+    G.banner("prefill N=4096, 64 query heads over 8 K/V heads, rows sampled")
+    wl = W.build("pf_gqa", 5, heads=8, head_dim=128, page_size=256, lens=[4096],
+                 q_lens=[4096], causal=True, shuffle=True, device="cuda", poison=True,
+                 q_heads=64)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    q, k, v, table = G.host_inputs(wl, call, [0])
+    k = np.repeat(k, 8, axis=2)
+    v = np.repeat(v, 8, axis=2)
+    rows = {0: G.spread_rows(4096, 24, seed=6)}
+    ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, True,
+                              wl.scale, rows=rows)
+    G.compare(G.bf16_out_to_f64(out), ref, "prefill_4096 grouped 64/8")
+
+
 def test_prefill_32k_sampled():
     G.banner("prefill_32k full size, rows sampled (all heads)")
     wl = W.prefill_32k(device="cuda", poison=True)

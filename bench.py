@@ -359,10 +359,6 @@ def cpu_baseline_decode(wl, call, budget_s=10.0):
             sel = torch.as_tensor(pages.astype("int64"), device=wl.k_pool.device)
             k = W.to_host_bits(wl.k_pool.index_select(0, sel))
             v = W.to_host_bits(wl.v_pool.index_select(0, sel))
-            rep = wl.num_q_heads // wl.heads
-            if rep > 1:  # grouped heads: the oracle is per head, so K/V heads repeat
-                k = np.repeat(k, rep, axis=2)
-                v = np.repeat(v, rep, axis=2)
             table = np.arange(n, dtype=np.int64)[None, :]
             t0 = time.perf_counter()
             OA.paged_decode(q[b:b + 1], k, v, table, call.seq_lens_host[b:b + 1], wl.scale)
@@ -393,10 +389,6 @@ def cpu_baseline_prefill(wl, call, budget_s=15.0):
     q = W.to_host_bits(call.q)
     k = W.to_host_bits(wl.k_pool)
     v = W.to_host_bits(wl.v_pool)
-    rep = wl.num_q_heads // wl.heads
-    if rep > 1:  # grouped heads: the oracle is per head, so K/V heads repeat
-        k = np.repeat(k, rep, axis=2)
-        v = np.repeat(v, rep, axis=2)
     q_len = int(call.q_start_host[1] - call.q_start_host[0])
     L = int(call.seq_lens_host[0])
     n_rows, spent, pairs = 16, 0.0, 0

@@ -38,11 +38,19 @@ Readings where the pages leave a step open:
     the previous w tokens): with window w >= 1 a query at position p sees the w
     keys p - w + 1 .. p (its own key included); window 0 means no window.  Only
     meaningful together with causal attention.
+  * Grouped heads ("Flash Attention: Fast, Memory-Efficient Attention for LLMs",
+    section "Attention Variants: MHA, GQA, MQA"): with H_q query heads over H_kv
+    K/V heads, consecutive blocks of g = H_q / H_kv query heads share one K/V
+    head (the page's flowchart puts query heads 1-4 in K/V group 1 and 5-8 in
+    group 2); zero-based, query head h reads K/V head h // g.  H_kv = H_q is
+    multi-head attention, H_kv = 1 multi-query attention.  The K/V head count is
+    the pools' head dimension, the query head count that of q.
 
 Inputs are raw bf16 bit patterns (uint16 arrays).  Decoding them to fp64 is
 exact.  The output stays in fp64; nothing here rounds to bf16.
 
-Parity status: pinned (see tests/test_oracle_pins.py for each pin).
+Parity status: pinned (see tests/test_oracle_pins.py for each pin), including the
+grouped-head mapping and the sampled evaluation (rows= / seqs=).
 """
 from __future__ import annotations
 
@@ -106,6 +114,31 @@ def gather_sequence(pool_bits: np.ndarray, block_table_row: Sequence[int],
     return bf16_to_f64(rows)
 
 
+def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """K/V head read by query head h (zero-based) when num_q_heads query heads share
+    num_kv_heads K/V heads in consecutive equal groups.
+
+    "Flash Attention: Fast, Memory-Efficient Attention for LLMs", section "Attention
+    Variants: MHA, GQA, MQA": 8 query heads in 2 K/V groups, heads 1-4 in the first
+    and 5-8 in the second, so a group is a run of g = num_q_heads / num_kv_heads
+    adjacent query heads.
+    """
+    if num_kv_heads < 1 or num_q_heads % num_kv_heads:
+        raise ValueError(f"{num_q_heads} query heads do not split into {num_kv_heads} "
+                         "equal K/V groups")
+    group = num_q_heads // num_kv_heads
+    return h // group
+
+
+def row_positions(seq_len: int, q_len: int, local_rows) -> np.ndarray:
+    """Absolute positions of local query rows of a q_len-row chunk over seq_len keys.
+
+    The chunk is the last q_len tokens of the sequence (bottom-right causal
+    alignment; see the module docstring), so local row i sits at seq_len - q_len + i.
+    """
+    return int(seq_len) - int(q_len) + np.asarray(local_rows, dtype=np.int64)
+
+
 def visible_mask(positions: np.ndarray, seq_len: int, causal: bool,
                  window: int = 0) -> np.ndarray:
     """Boolean [rows, L]: key t is visible to a query at absolute position p.
@@ -158,20 +191,22 @@ def attend(q_rows: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
            positions: np.ndarray, causal: bool, scale: float, window: int = 0):
     """Attention of some query rows of one sequence over its gathered keys.
 
-    q_rows [r, H, d] fp64, k_seq / v_seq [L, H, d] fp64, positions [r] absolute.
-    Returns (O [r, H, d] fp64, lse [r, H] fp64 natural-log sum of exp).
+    q_rows [r, H_q, d] fp64, k_seq / v_seq [L, H_kv, d] fp64 (H_q a multiple of
+    H_kv; query head h reads K/V head kv_head_of(h, H_q, H_kv)), positions [r]
+    absolute.  Returns (O [r, H_q, d] fp64, lse [r, H_q] fp64 natural-log sum of exp).
     """
     r, heads, d = q_rows.shape
-    seq_len = k_seq.shape[0]
+    seq_len, kv_heads = k_seq.shape[0], k_seq.shape[1]
     out = np.empty((r, heads, d), dtype=np.float64)
     lse = np.empty((r, heads), dtype=np.float64)
     for h in range(heads):
+        hk = kv_head_of(h, heads, kv_heads)
         for r0 in range(0, r, ROW_BLOCK):
             r1 = min(r, r0 + ROW_BLOCK)
             mask = visible_mask(positions[r0:r1], seq_len, causal, window)
-            s = scores(q_rows[r0:r1, h, :], k_seq[:, h, :], scale)
+            s = scores(q_rows[r0:r1, h, :], k_seq[:, hk, :], scale)
             p, row_lse = softmax_rows(s, mask)
-            out[r0:r1, h, :] = weighted_values(p, v_seq[:, h, :])
+            out[r0:r1, h, :] = weighted_values(p, v_seq[:, hk, :])
             lse[r0:r1, h] = row_lse
     return out, lse
 
@@ -180,15 +215,17 @@ def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_sta
                   causal: bool, scale: float, rows: Optional[dict] = None, window: int = 0):
     """Prefill (or chunked prefill) over a paged cache.
 
-    q_bits       uint16 [total_q, H, d]; rows of sequence b are q_start[b]..q_start[b+1]-1
-    k/v_pool_bits uint16 [num_pages, page_size, H, d]
+    q_bits       uint16 [total_q, H_q, d]; rows of sequence b are q_start[b]..q_start[b+1]-1
+    k/v_pool_bits uint16 [num_pages, page_size, H_kv, d]; H_q a multiple of H_kv
     block_table  int [batch, max_pages_per_seq]
     seq_lens     int [batch]: L_b, the KV length including this chunk
     scale        the fp32 scale value (widened exactly)
     rows         optional {b: array of local row indices} to evaluate only some rows
     window       sliding-window length w (0: none); needs causal
 
-    Returns (O fp64 [total_q, H, d] with NaN where not evaluated, lse [total_q, H]).
+    Returns (O fp64 [total_q, H_q, d] with NaN where not evaluated, lse [total_q, H_q]).
+    Evaluating only some rows gives, for those rows, what the full evaluation gives:
+    each row is computed from its own query, position and the sequence's keys.
     """
     q_bits = np.asarray(q_bits)
     total_q, heads, d = q_bits.shape
@@ -209,7 +246,7 @@ def paged_prefill(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_sta
         local = np.arange(q_len) if rows is None else np.asarray(rows[b], dtype=np.int64)
         k_seq = gather_sequence(k_pool_bits, block_table[b], seq_len, page_size)
         v_seq = gather_sequence(v_pool_bits, block_table[b], seq_len, page_size)
-        positions = seq_len - q_len + local
+        positions = row_positions(seq_len, q_len, local)
         q_rows = bf16_to_f64(q_bits[start + local])
         o, l = attend(q_rows, k_seq, v_seq, positions, causal, scale, window)
         out[start + local] = o
@@ -222,8 +259,8 @@ def paged_decode(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, scale:
     """Decode: one query token per sequence over all L_b cached keys (itself included),
     or over the last `window` of them when window > 0.
 
-    q_bits uint16 [batch, H, d].  Returns (O fp64 [batch, H, d], lse [batch, H]);
-    sequences not in `seqs` are left NaN.
+    q_bits uint16 [batch, H_q, d], pools [num_pages, page_size, H_kv, d].  Returns
+    (O fp64 [batch, H_q, d], lse [batch, H_q]); sequences not in `seqs` are left NaN.
     """
     q_bits = np.asarray(q_bits)
     batch, heads, d = q_bits.shape
@@ -269,7 +306,8 @@ def kv_append(k_pool_bits: np.ndarray, v_pool_bits: np.ndarray, block_table,
 
 
 __all__ = [
-    "bf16_to_f64", "pages_needed", "locate_token", "gather_sequence", "visible_mask",
+    "bf16_to_f64", "pages_needed", "locate_token", "gather_sequence", "kv_head_of",
+    "row_positions", "visible_mask",
     "scores", "softmax_rows", "weighted_values", "attend", "paged_prefill", "paged_decode",
     "kv_append", "ROW_BLOCK",
 ]

@@ -49,30 +49,40 @@ def bf16_out_to_f64(out: torch.Tensor) -> np.ndarray:
     return OA.bf16_to_f64(W.to_host_bits(out))
 
 
+def compact_pages(block_table_host, seq_lens_host, seqs, page_size):
+    """The pages the given sequences read, sorted and without repeats, and the block
+    table rewritten onto positions in that list (-1 for everything else)."""
+    pages = []
+    for b in seqs:
+        n = OA.pages_needed(int(seq_lens_host[b]), page_size)
+        pages.extend(int(p) for p in block_table_host[b, :n])
+    uniq = sorted(set(pages))
+    index = {p: i for i, p in enumerate(uniq)}
+    table = np.full_like(block_table_host, -1)
+    for b in seqs:
+        n = OA.pages_needed(int(seq_lens_host[b]), page_size)
+        table[b, :n] = [index[int(p)] for p in block_table_host[b, :n]]
+    return uniq, table
+
+
 def host_inputs(wl: W.Workload, call: W.AttnCall, seqs):
     """Host copies (uint16 bit patterns) of the pages the given sequences read, with
     the block table rewritten onto the compacted page list; the oracle then gathers
-    the very same bytes the kernel reads."""
-    ps = wl.page_size
-    pages = []
-    for b in seqs:
-        n = OA.pages_needed(int(call.seq_lens_host[b]), ps)
-        pages.extend(int(p) for p in call.block_table_host[b, :n])
-    uniq = sorted(set(pages))
-    index = {p: i for i, p in enumerate(uniq)}
+    the very same bytes the kernel reads.  (The compaction changes no output bit:
+    tests/test_sampled_oracle_cpu.py.)"""
+    uniq, table = compact_pages(call.block_table_host, call.seq_lens_host, seqs,
+                                wl.page_size)
     sel = torch.tensor(uniq, dtype=torch.long, device=wl.k_pool.device)
     k = W.to_host_bits(wl.k_pool.index_select(0, sel))
     v = W.to_host_bits(wl.v_pool.index_select(0, sel))
-    table = np.full_like(call.block_table_host, -1)
-    for b in seqs:
-        n = OA.pages_needed(int(call.seq_lens_host[b]), ps)
-        table[b, :n] = [index[int(p)] for p in call.block_table_host[b, :n]]
     q = W.to_host_bits(call.q)
     return q, k, v, table
 
 
-def oracle_for(wl: W.Workload, call: W.AttnCall, seqs=None, rows=None):
-    """fp64 reference of (some of) a call's outputs.  rows: {b: local row indices}."""
+def oracle_for(wl: W.Workload, call: W.AttnCall, seqs=None, rows=None, window=0):
+    """fp64 reference of (some of) a call's outputs.  rows: {b: local row indices}.
+    Grouped heads need nothing here: the oracle reads the K/V head count from the
+    pools and maps query heads onto K/V heads itself."""
     if seqs is None:
         seqs = list(range(call.batch)) if rows is None else sorted(rows)
     q, k, v, table = host_inputs(wl, call, seqs)
@@ -80,9 +90,10 @@ def oracle_for(wl: W.Workload, call: W.AttnCall, seqs=None, rows=None):
         sel_rows = rows if rows is not None else {b: np.arange(
             call.q_start_host[b + 1] - call.q_start_host[b]) for b in seqs}
         ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host,
-                                  call.causal, wl.scale, rows=sel_rows)
+                                  call.causal, wl.scale, rows=sel_rows, window=window)
     else:
-        ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, seqs=seqs)
+        ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, seqs=seqs,
+                                 window=window)
     return ref
 
 

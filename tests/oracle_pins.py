@@ -39,8 +39,9 @@ def bits_of_int(v):
 
 
 def random_paged_case(rng, batch, heads, d, page_size, lens, q_lens, extra_pages=3,
-                      sigma=1.0, poison=True):
-    """A tiny paged problem with a shuffled pool, NaN in every unread slot."""
+                      sigma=1.0, poison=True, q_heads=None):
+    """A tiny paged problem with a shuffled pool, NaN in every unread slot.  heads is
+    the pools' K/V head count; q_heads (default heads) the query head count."""
     n_pages = [A.pages_needed(L, page_size) for L in lens]
     num_pages = sum(n_pages) + extra_pages
     perm = rng.permutation(num_pages)
@@ -62,19 +63,23 @@ def random_paged_case(rng, batch, heads, d, page_size, lens, q_lens, extra_pages
         k[~used] = nan
         v[~used] = nan
     q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
-    q = to_bf16_bits(rng.normal(0.0, sigma, (int(q_start[-1]), heads, d)))
+    q = to_bf16_bits(rng.normal(0.0, sigma, (int(q_start[-1]), q_heads or heads, d)))
     return dict(q=q, k=k, v=v, table=table, lens=np.array(lens), q_start=q_start)
 
 
-def brute_force(q, k, v, table, lens, q_start, causal, scale, window=0):
+def brute_force(q, k, v, table, lens, q_start, causal, scale, window=0, kv_of=None):
     """Scalar Python loops with math.exp; walks each sequence's pages in table order.
 
     Written independently of oracle.attention: no numpy arithmetic, and the
     keys of a sequence are collected page by page (slot o of the j-th listed
     page is token j*page_size + o) instead of by dividing token positions.
+    kv_of: explicit list, query head -> the K/V head it reads (default: the same
+    head, multi-head attention).
     """
     page_size = k.shape[1]
     heads, d = q.shape[1], q.shape[2]
+    if kv_of is None:
+        kv_of = list(range(heads))
     kf = k.astype(np.uint32) << 16
     vf = v.astype(np.uint32) << 16
     kf = kf.view(np.float32).astype(np.float64).tolist()
@@ -100,10 +105,11 @@ def brute_force(q, k, v, table, lens, q_start, causal, scale, window=0):
             first = max(0, last - window + 1) if window else 0
             for h in range(heads):
                 s = []
+                hk = kv_of[h]
                 for t in range(first, last + 1):
                     acc = 0.0
                     for c in range(d):
-                        acc += qf[row][h][c] * keys[t][h][c]
+                        acc += qf[row][h][c] * keys[t][hk][c]
                     s.append(scale * acc)
                 mx = max(s)
                 e = [math.exp(x - mx) for x in s]
@@ -111,7 +117,7 @@ def brute_force(q, k, v, table, lens, q_start, causal, scale, window=0):
                 for c in range(d):
                     acc = 0.0
                     for t in range(first, last + 1):
-                        acc += e[t - first] * vals[t][h][c]
+                        acc += e[t - first] * vals[t][hk][c]
                     out[row][h][c] = acc / tot
     return np.array(out)
 
@@ -510,6 +516,126 @@ def pin_shared_prefix_pages_hold_both_sequences(seed=10) -> bool:
                 np.array_equal(cv[untouched], v[untouched]))
 
 
+def _flowchart_groups():
+    """The flowchart's membership lists, zero-based: query head -> K/V head."""
+    g = load_golden("gqa_attention_variants_flowchart.json")["gqa_flowchart"]
+    kv_of = [None] * g["n_q_heads"]
+    for group, members in g["groups"].items():
+        for head in members:
+            kv_of[head - 1] = int(group) - 1
+    return g, kv_of
+
+
+def pin_gqa_flowchart_mapping() -> bool:
+    """The page's grouped-query flowchart, exactly: with 8 query heads over 2 K/V
+    heads, heads 1-4 read group 1 and 5-8 read group 2; the 4x and 8x KV-cache
+    reductions are the group sizes; MQA maps every head to the one K/V head and MHA
+    maps each head to its own."""
+    g, kv_of = _flowchart_groups()
+    nq, nkv = g["n_q_heads"], g["n_kv_heads"]
+    if [A.kv_head_of(h, nq, nkv) for h in range(nq)] != kv_of:
+        return False
+    if nq // nkv != g["kv_cache_reduction_vs_mha"]:
+        return False
+    big = load_golden("gqa_attention_variants_flowchart.json")["gqa_64_over_8"]
+    got = [A.kv_head_of(h, big["n_q_heads"], big["n_kv_heads"]) for h in range(big["n_q_heads"])]
+    sizes = [got.count(j) for j in range(big["n_kv_heads"])]
+    if sizes != [big["kv_cache_reduction_vs_mha"]] * big["n_kv_heads"] or got != sorted(got):
+        return False
+    if any(A.kv_head_of(h, 7, 1) != 0 for h in range(7)):
+        return False
+    return all(A.kv_head_of(h, 5, 5) == h for h in range(5))
+
+
+def pin_gqa_brute_force(seed=11) -> bool:
+    """Grouped heads against scalar loops that read the flowchart's membership lists
+    (8 query heads, 2 K/V heads), causal chunks, non-causal, and decode."""
+    _, kv_of = _flowchart_groups()
+    rng = np.random.default_rng(seed)
+    case = random_paged_case(rng, 2, 2, 3, 4, [9, 6], [4, 6], q_heads=8)
+    scale = float(np.float32(0.43))
+    for causal in (True, False):
+        want = brute_force(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                           case["q_start"], causal, scale, kv_of=kv_of)
+        got, _ = A.paged_prefill(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                                 case["q_start"], causal, scale)
+        if not np.all(np.isfinite(got)) or np.max(np.abs(got - want)) > 1e-13:
+            return False
+    last_rows = case["q_start"][1:] - 1
+    dec, _ = A.paged_decode(case["q"][last_rows], case["k"], case["v"], case["table"],
+                            case["lens"], scale)
+    want = brute_force(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                       case["q_start"], True, scale, kv_of=kv_of)
+    return bool(np.max(np.abs(dec - want[last_rows])) < 1e-13)
+
+
+def pin_gqa_equals_replicated_heads(seed=12) -> bool:
+    """Grouped attention is multi-head attention over pools in which every query head
+    has its own copy of the K/V head the flowchart assigns it: bit-identical."""
+    _, kv_of = _flowchart_groups()
+    rng = np.random.default_rng(seed)
+    case = random_paged_case(rng, 2, 2, 8, 4, [11, 7], [5, 7], q_heads=8)
+    k_rep = case["k"][:, :, kv_of, :]
+    v_rep = case["v"][:, :, kv_of, :]
+    for causal, window in ((True, 0), (False, 0), (True, 3)):
+        grouped, _ = A.paged_prefill(case["q"], case["k"], case["v"], case["table"],
+                                     case["lens"], case["q_start"], causal, 0.3, window=window)
+        mha, _ = A.paged_prefill(case["q"], k_rep, v_rep, case["table"], case["lens"],
+                                 case["q_start"], causal, 0.3, window=window)
+        if not np.array_equal(grouped, mha):
+            return False
+    dq = case["q"][case["q_start"][1:] - 1]
+    grouped, _ = A.paged_decode(dq, case["k"], case["v"], case["table"], case["lens"], 0.3)
+    mha, _ = A.paged_decode(dq, k_rep, v_rep, case["table"], case["lens"], 0.3)
+    return bool(np.array_equal(grouped, mha))
+
+
+def pin_sampled_rows_match_full(seed=13) -> bool:
+    """Evaluating only some query rows (the sampled evaluation used at full sizes) gives
+    those rows of the full evaluation, NaN elsewhere: chunks whose rows sit at L - q_len
+    and later, rows not starting at 0, sequences left out, windows, grouped heads."""
+    rng = np.random.default_rng(seed)
+    case = random_paged_case(rng, 3, 2, 4, 4, [13, 9, 17], [6, 9, 5], q_heads=4)
+    rows = {0: np.array([5, 1, 3]), 2: np.array([4, 0])}
+    for causal, window in ((True, 0), (False, 0), (True, 4)):
+        full, full_lse = A.paged_prefill(case["q"], case["k"], case["v"], case["table"],
+                                         case["lens"], case["q_start"], causal, 0.35,
+                                         window=window)
+        part, part_lse = A.paged_prefill(case["q"], case["k"], case["v"], case["table"],
+                                         case["lens"], case["q_start"], causal, 0.35,
+                                         rows=rows, window=window)
+        picked = np.zeros(len(case["q"]), dtype=bool)
+        for b, rr in rows.items():
+            picked[case["q_start"][b] + rr] = True
+        if not np.all(np.isnan(part[~picked])) or not np.all(np.isfinite(part[picked])):
+            return False
+        # BLAS may block a different number of rows differently: equal to rounding
+        if np.max(np.abs(part[picked] - full[picked])) > 1e-13:
+            return False
+        if np.max(np.abs(part_lse[picked] - full_lse[picked])) > 1e-13:
+            return False
+    return True
+
+
+def pin_sampled_seqs_match_full(seed=14) -> bool:
+    """Decode over some sequences gives those sequences of the full decode, NaN
+    elsewhere (grouped heads, with and without a window)."""
+    rng = np.random.default_rng(seed)
+    case = random_paged_case(rng, 4, 2, 4, 4, [13, 9, 1, 17], [1, 1, 1, 1], q_heads=6)
+    seqs = [3, 1]
+    for window in (0, 5):
+        full, _ = A.paged_decode(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                                 0.4, window=window)
+        part, _ = A.paged_decode(case["q"], case["k"], case["v"], case["table"], case["lens"],
+                                 0.4, seqs=seqs, window=window)
+        rest = [b for b in range(4) if b not in seqs]
+        if not np.all(np.isnan(part[rest])):
+            return False
+        if np.max(np.abs(part[seqs] - full[seqs])) > 1e-13:
+            return False
+    return True
+
+
 ALL_PINS = [
     pin_practical_example_translation,
     pin_practical_example_gather,
@@ -525,6 +651,11 @@ ALL_PINS = [
     pin_kv_append_round_trip,
     pin_logical_cache_fork_isolation,
     pin_shared_prefix_pages_hold_both_sequences,
+    pin_gqa_flowchart_mapping,
+    pin_gqa_brute_force,
+    pin_gqa_equals_replicated_heads,
+    pin_sampled_rows_match_full,
+    pin_sampled_seqs_match_full,
 ]
 
 

@@ -10,7 +10,6 @@ import torch
 from exact_tiled_attention_pa_amd import binding as B
 from exact_tiled_attention_pa_amd import workloads as W
 from tests import gpu_helpers as G
-from tests.test_gpu_parity import oracle_grouped
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +49,7 @@ def test_decode_step_replays_from_a_graph():
         run(out_e)                      # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(_bits(out_g), _bits(out_e)), f"replay {rep}"
-    G.compare(G.bf16_out_to_f64(out_g), oracle_grouped(wl, call, 8, 4),
+    G.compare(G.bf16_out_to_f64(out_g), G.oracle_for(wl, call),
               "graph decode, last replay")
 
 

@@ -208,9 +208,9 @@ class DeviceCache:
         for s in live:
             lk, lv = self.ref.rows(s)
             L = lk.shape[0]
-            kk = np.repeat(OA.bf16_to_f64(lk), 2, axis=1)   # query head h reads KV head h // 2
-            vv = np.repeat(OA.bf16_to_f64(lv), 2, axis=1)
-            o, _ = OA.attend(qf[s:s + 1], kk, vv, np.array([L - 1]), True, scale)
+            # two query heads per K/V head: the oracle maps them onto the K/V heads
+            o, _ = OA.attend(qf[s:s + 1], OA.bf16_to_f64(lk), OA.bf16_to_f64(lv),
+                             np.array([L - 1]), True, scale)
             ref[s] = o[0]
         G.compare(got, ref, f"block-manager decode over {len(live)} sequences")
 

@@ -57,27 +57,8 @@ def test_prefill_small_element_wise(d, ps, causal, hq, hkv, lens, q_lens):
                   .to(torch.bfloat16))
     out = G.run_call(wl, call)
     torch.cuda.synchronize()
-    ref = oracle_grouped(wl, call, hq, hkv)
+    ref = G.oracle_for(wl, call)
     G.compare(G.bf16_out_to_f64(out), ref, f"prefill d={d} ps={ps} causal={causal}")
-
-
-def oracle_grouped(wl, call, hq, hkv):
-    """Oracle for grouped heads: query head h reads K/V head h // (hq // hkv); the
-    oracle itself is per-head MHA, so K/V heads are repeated on the host."""
-    if hq == hkv:
-        return G.oracle_for(wl, call)
-    from oracle import attention as OA
-    seqs = list(range(call.batch))
-    q, k, v, table = G.host_inputs(wl, call, seqs)
-    rep = hq // hkv
-    k = np.repeat(k, rep, axis=2)
-    v = np.repeat(v, rep, axis=2)
-    if call.kind == "prefill":
-        ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host,
-                                  call.causal, wl.scale)
-    else:
-        ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale)
-    return ref
 
 
 DECODE_CASES = [
@@ -113,8 +94,7 @@ def test_decode_small_element_wise(d, ps, hq, hkv, lens):
     call = wl.calls[0]
     out = G.run_call(wl, call)
     torch.cuda.synchronize()
-    G.compare(G.bf16_out_to_f64(out), oracle_grouped(wl, call, hq, hkv),
-              f"decode d={d} ps={ps}")
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), f"decode d={d} ps={ps}")
 
 
 @pytest.mark.parametrize("hq", [4, 16])
@@ -143,18 +123,8 @@ def test_decode_64_gqa8_sampled():
     torch.cuda.synchronize()
     lens = call.seq_lens_host
     seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 21, 40})
-    ref = oracle_grouped_seqs(wl, call, seqs)
+    ref = G.oracle_for(wl, call, seqs=seqs)
     G.compare(G.bf16_out_to_f64(out), ref, "decode_64_gqa8")
-
-
-def oracle_grouped_seqs(wl, call, seqs):
-    from oracle import attention as OA
-    q, k, v, table = G.host_inputs(wl, call, seqs)
-    rep = wl.num_q_heads // wl.heads
-    k = np.repeat(k, rep, axis=2)
-    v = np.repeat(v, rep, axis=2)
-    ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, seqs=seqs)
-    return ref
 
 
 def test_decode_64_sampled():
@@ -184,7 +154,6 @@ def test_prefill_4096_sampled(causal):
 def test_prefill_4096_grouped_heads_sampled():
     """64 query heads over 8 K/V heads at N=4096, causal, shuffled pages of 256: the
     grouped-head prefill at full size, rows sampled, all query heads checked."""
-    from oracle import attention as OA
     G.banner("prefill N=4096, 64 query heads over 8 K/V heads, rows sampled")
     wl = W.build("pf_gqa", 5, heads=8, head_dim=128, page_size=256, lens=[4096],
                  q_lens=[4096], causal=True, shuffle=True, device="cuda", poison=True,
@@ -192,12 +161,8 @@ def test_prefill_4096_grouped_heads_sampled():
     call = wl.calls[0]
     out = G.run_call(wl, call)
     torch.cuda.synchronize()
-    q, k, v, table = G.host_inputs(wl, call, [0])
-    k = np.repeat(k, 8, axis=2)
-    v = np.repeat(v, 8, axis=2)
     rows = {0: G.spread_rows(4096, 24, seed=6)}
-    ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, True,
-                              wl.scale, rows=rows)
+    ref = G.oracle_for(wl, call, rows=rows)
     G.compare(G.bf16_out_to_f64(out), ref, "prefill_4096 grouped 64/8")
 
 
@@ -423,10 +388,7 @@ def test_prefill_sliding_window(d, ps, lens, q_lens, window):
     B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, True,
                  wl.scale, out, call.q_start, call.max_q_len, window=window)
     torch.cuda.synchronize()
-    from oracle import attention as OA
-    q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
-    ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, True,
-                              wl.scale, window=window)
+    ref = G.oracle_for(wl, call, window=window)
     G.compare(G.bf16_out_to_f64(out), ref, f"prefill window={window}")
 
 
@@ -443,10 +405,7 @@ def test_decode_sliding_window(window, hq):
     B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale, out,
                 ws, window=window)
     torch.cuda.synchronize()
-    from oracle import attention as OA
-    q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
-    k, v = np.repeat(k, hq // 4, axis=2), np.repeat(v, hq // 4, axis=2)
-    ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, window=window)
+    ref = G.oracle_for(wl, call, window=window)
     G.compare(G.bf16_out_to_f64(out), ref, f"decode window={window} Hq={hq}")
 
 
@@ -481,7 +440,7 @@ def test_prefill_ragged_batch_with_empty_chunks(causal, hq):
     B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, causal,
                  wl.scale, out, call.q_start, call.max_q_len)
     torch.cuda.synchronize()
-    ref = oracle_grouped(wl, call, hq, 2)
+    ref = G.oracle_for(wl, call)
     G.compare(G.bf16_out_to_f64(out), ref, f"ragged causal={causal} Hq={hq}")
 
 
@@ -509,11 +468,7 @@ def test_prefill_window_grouped_heads():
     B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, True,
                  wl.scale, out, call.q_start, call.max_q_len, window=100)
     torch.cuda.synchronize()
-    from oracle import attention as OA
-    q, k, v, table = G.host_inputs(wl, call, [0, 1])
-    k, v = np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2)
-    ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, True,
-                              wl.scale, window=100)
+    ref = G.oracle_for(wl, call, window=100)
     G.compare(G.bf16_out_to_f64(out), ref, "prefill window=100 grouped")
 
 
@@ -527,7 +482,7 @@ def test_decode_half_million_token_sequence(hq):
     call = wl.calls[0]
     out = G.run_call(wl, call)
     torch.cuda.synchronize()
-    G.compare(G.bf16_out_to_f64(out), oracle_grouped(wl, call, hq, 1), f"decode long Hq={hq}")
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), f"decode long Hq={hq}")
 
 
 # ----------------------------------------------------------------- kernel against kernel
@@ -549,7 +504,7 @@ def test_grouped_decode_kernel_agrees_with_per_head_kernel():
     ws = B.decode_workspace(call.q, k_rep, call.block_table)
     B.pa_decode(call.q, k_rep, v_rep, call.block_table, call.seq_lens, wl.scale, out, ws)
     torch.cuda.synchronize()
-    ref = oracle_grouped(wl, call, 8, 2)
+    ref = G.oracle_for(wl, call)
     G.compare(G.bf16_out_to_f64(grouped), ref, "grouped kernel")
     G.compare(G.bf16_out_to_f64(out), ref, "per-head kernel")
     G.compare(G.bf16_out_to_f64(grouped), G.bf16_out_to_f64(out), "grouped vs per-head",

@@ -62,10 +62,6 @@ def prefill_case(seed):
     return d, ps, hkv, hkv * g, lens, q_lens, causal, window
 
 
-def _repeat_heads(k, v, rep):
-    return (np.repeat(k, rep, axis=2), np.repeat(v, rep, axis=2)) if rep > 1 else (k, v)
-
-
 @pytest.mark.parametrize("seed", range(16))
 def test_random_decode(seed):
     d, ps, hkv, hq, lens, window = decode_case(seed)
@@ -80,7 +76,6 @@ def test_random_decode(seed):
                 ws, window=window)
     torch.cuda.synchronize()
     q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
-    k, v = _repeat_heads(k, v, hq // hkv)
     ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale, window=window)
     G.compare(G.bf16_out_to_f64(out), ref, f"random decode seed={seed}")
 
@@ -100,7 +95,6 @@ def test_random_prefill(seed):
                      wl.scale, out, call.q_start, call.max_q_len, window=window)
     torch.cuda.synchronize()
     q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
-    k, v = _repeat_heads(k, v, hq // hkv)
     ref, _ = OA.paged_prefill(q, k, v, table, call.seq_lens_host, call.q_start_host, causal,
                               wl.scale, window=window)
     G.compare(G.bf16_out_to_f64(out), ref, f"random prefill seed={seed}")
@@ -118,7 +112,6 @@ def test_many_short_sequences_decode_and_prefill():
     out = G.run_call(wl, call)
     torch.cuda.synchronize()
     q, k, v, table = G.host_inputs(wl, call, list(range(call.batch)))
-    k, v = _repeat_heads(k, v, 2)
     ref, _ = OA.paged_decode(q, k, v, table, call.seq_lens_host, wl.scale)
     G.compare(G.bf16_out_to_f64(out), ref, "many short decode sequences")
 

@@ -96,12 +96,27 @@ def _append_skips_v(k_pool_bits, v_pool_bits, block_table, seq_ids, positions, k
     return k, np.array(v_pool_bits, copy=True)
 
 
+def _heads_interleaved(h, num_q_heads, num_kv_heads):
+    # query heads dealt round-robin over the K/V heads instead of in adjacent groups
+    return h % num_kv_heads
+
+
+def _heads_divided_by_kv_count(h, num_q_heads, num_kv_heads):
+    # divides by the K/V head count instead of the group size
+    return h // num_kv_heads
+
+
+def _positions_from_sample_index(seq_len, q_len, local_rows):
+    # numbers the sampled rows 0, 1, ... instead of using their row indices
+    return int(seq_len) - int(q_len) + np.arange(len(local_rows))
+
+
 _ORIG_FORK = LC.LogicalCache.fork
 _ORIG_COPY = LC.copy_pages
 
 _ORIG = {name: getattr(A, name) for name in
          ("locate_token", "visible_mask", "scores", "softmax_rows", "weighted_values", "bf16_to_f64",
-          "kv_append")}
+          "kv_append", "kv_head_of", "row_positions")}
 
 MUTANTS = [
     ("locate_token", _swap_quotient_remainder),
@@ -120,6 +135,9 @@ MUTANTS = [
     ("LogicalCache.fork", _fork_aliases_parent),
     ("LogicalCache.fork", _fork_drops_last_row),
     ("copy_pages", _copy_pages_reversed),
+    ("kv_head_of", _heads_interleaved),
+    ("kv_head_of", _heads_divided_by_kv_count),
+    ("row_positions", _positions_from_sample_index),
 ]
 
 

@@ -13,6 +13,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +43,88 @@ class PagedAttnError(RuntimeError):
         super().__init__(f"{status_string(status)} -- {detail}")
         self.status = status
         self.detail = detail
+
+
+class ContractError(ValueError):
+    """A block table, length or chunk offset breaks the device-array contract of
+    pagedattn.h (raised by the opt-in host-side check, before anything is launched)."""
+
+
+# Opt-in host-side check of the device-array contract before each attention launch
+# (PA_CHECK_CONTRACT=1 in the environment, or set_contract_check(True)).  It copies
+# the block table, lengths and chunk offsets to the host, which synchronises with
+# the device: a debugging aid, not for timed or captured work.
+_check_contract = os.environ.get("PA_CHECK_CONTRACT", "0") not in ("", "0")
+
+
+def set_contract_check(enabled: bool) -> None:
+    global _check_contract
+    _check_contract = bool(enabled)
+
+
+def _host_ints(x):
+    if isinstance(x, torch.Tensor):
+        return x.detach().to("cpu").numpy().astype(np.int64)
+    return np.asarray(x, dtype=np.int64)
+
+
+def contract_violations(block_table, seq_lens, num_pages: int, page_size: int,
+                        q_start=None, max_q_len=None, total_q=None, max_report: int = 8):
+    """Host-side check of the device-array contract stated in pagedattn.h: for each
+    sequence b with KV length L_b, 0 <= L_b <= max_pages_per_seq * page_size and
+    0 <= block_table[b, p] < num_pages for every p < ceil(L_b / page_size), the pages
+    the kernels read ("What is Paged FlashAttention?", "Practical example": physical
+    page = block_table[pos // page_size]).  With chunk offsets (prefill), q_start
+    starts at 0, never decreases, stays within total_q rows, and every
+    q_len_b = q_start[b+1] - q_start[b] is at most L_b and at most max_q_len.
+    Accepts host arrays or tensors (copied to the host).  Returns a list of
+    messages, empty when the arrays keep the contract."""
+    bt = _host_ints(block_table)
+    lens = _host_ints(seq_lens).reshape(-1)
+    bad = []
+    if bt.ndim != 2 or bt.shape[0] < lens.size:
+        return [f"block_table has shape {bt.shape}, expected [>= {lens.size}, max_pages]"]
+    max_pages = bt.shape[1]
+    for b, L in enumerate(lens.tolist()):
+        if L < 0 or L > max_pages * page_size:
+            bad.append(f"sequence {b}: length {L} outside [0, {max_pages * page_size}] "
+                       f"({max_pages} table entries of {page_size} tokens)")
+            continue
+        n = -(-L // page_size)
+        row = bt[b, :n]
+        out = np.nonzero((row < 0) | (row >= num_pages))[0]
+        for p in out[:2].tolist():
+            bad.append(f"sequence {b}: logical page {p} maps to physical page {int(row[p])}, "
+                       f"outside the pool of {num_pages} pages")
+    if q_start is not None:
+        qs = _host_ints(q_start).reshape(-1)
+        if qs.size != lens.size + 1:
+            bad.append(f"q_start has {qs.size} entries, expected {lens.size + 1}")
+        else:
+            if qs[0] != 0:
+                bad.append(f"q_start[0] is {int(qs[0])}, expected 0")
+            if total_q is not None and qs[-1] > total_q:
+                bad.append(f"q_start[{lens.size}] = {int(qs[-1])} exceeds the {total_q} "
+                           "query rows")
+            for b in range(lens.size):
+                q_len = int(qs[b + 1] - qs[b])
+                if q_len < 0:
+                    bad.append(f"sequence {b}: q_start decreases ({int(qs[b])} -> "
+                               f"{int(qs[b + 1])})")
+                elif q_len > lens[b]:
+                    bad.append(f"sequence {b}: {q_len} query rows over only {int(lens[b])} keys")
+                elif max_q_len is not None and q_len > max_q_len:
+                    bad.append(f"sequence {b}: {q_len} query rows exceed max_q_len {max_q_len}")
+    return bad[:max_report]
+
+
+def _enforce_contract(block_table, seq_lens, k_pool, **kw):
+    if not _check_contract:
+        return
+    bad = contract_violations(block_table, seq_lens, int(k_pool.shape[0]),
+                              int(k_pool.shape[1]), **kw)
+    if bad:
+        raise ContractError("device-array contract broken: " + "; ".join(bad))
 
 
 class KVLayout(ctypes.Structure):
@@ -178,7 +261,10 @@ def pa_prefill(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_s
                max_q_len: int, stream=None, window: int = 0):
     """Paged (chunked) prefill: out[q_start[b]:q_start[b+1]] = attention of sequence b's
     query rows over its L_b = seq_lens[b] paged keys.  See pa_prefill in pagedattn.h;
-    window > 0 calls pa_prefill_window."""
+    window > 0 calls pa_prefill_window.  With the contract check on, the block table,
+    lengths and chunk offsets are checked on the host first (ContractError)."""
+    _enforce_contract(block_table, seq_lens, k_pool, q_start=q_start,
+                      max_q_len=int(max_q_len), total_q=int(q.shape[0]))
     _check_device_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
                           seq_lens=seq_lens, out=out, q_start=q_start)
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
@@ -223,6 +309,7 @@ def decode_workspace(q, k_pool, block_table) -> torch.Tensor:
 
 
 def _decode_checks(q, k_pool, v_pool, block_table, seq_lens, workspace, out=None):
+    _enforce_contract(block_table, seq_lens, k_pool)
     tensors = dict(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
                    seq_lens=seq_lens, workspace=workspace)
     if out is not None:

@@ -32,9 +32,11 @@ __device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) 
 // it (it would otherwise wait for these loads before unrelated LDS reads): callers
 // wait with explicit vmcnt waits, and must have no compiler-visible vector memory
 // loads of their own in flight while these are outstanding.
+// The LDS address goes in through an M0 operand, so the compiler writes M0 itself and
+// knows the asm reads it; the s_nop is the wait state between that write and the load.
 __device__ __forceinline__ void lds_load16(u32x4 rsrc, uint32_t lds_addr, int voffset) {
-  __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                       ::"s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory");
+  __asm__ __volatile__("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       ::"{m0}"(lds_addr), "v"(voffset), "s"(rsrc) : "memory");
 }
 
 // LDS byte address of a __shared__ object, as M0 takes it.

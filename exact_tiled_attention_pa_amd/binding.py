@@ -31,6 +31,7 @@ PA_ERR_CAPACITY = 6
 EXPORTED = (
     "pa_prefill", "pa_decode_workspace_bytes", "pa_decode_split_tokens", "pa_decode",
     "pa_decode_partial", "pa_decode_combine", "pa_prefill_window", "pa_decode_window",
+    "pa_decode_noalloc",
     "pa_kv_append", "pa_copy_pages", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence",
     "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append", "pa_bm_seq_len",
     "pa_bm_free_page_count", "pa_bm_ref_count", "pa_bm_export", "pa_bm_validate",
@@ -171,6 +172,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_prefill_window.restype = ctypes.c_int
     lib.pa_decode_window.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, vp, sz, lay, vp]
     lib.pa_decode_window.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, i32, lay, vp]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, lay, vp]
     lib.pa_kv_append.restype = ctypes.c_int
     lib.pa_copy_pages.argtypes = [vp, vp, vp, vp, i32, lay, vp]
@@ -345,6 +348,34 @@ def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace, s
                                       q.shape[1], _ptr(workspace), nbytes, ctypes.byref(lay),
                                       _stream(stream))
     _check(st)
+    return out
+
+
+# size of the library's static decode workspace (PA_NOALLOC_SCRATCH_BYTES in pagedattn.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pa_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, scale, out, stream=None):
+    """pa_decode without a workspace argument: the library keeps the split partials in
+    its own static device array (one per GPU), so the call allocates nothing.  Calls
+    that overlap on one GPU race; requests needing more than NOALLOC_SCRATCH_BYTES of
+    partials fail with PA_ERR_WORKSPACE."""
+    _enforce_contract(block_table, seq_lens, k_pool)
+    _check_device_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
+                          seq_lens=seq_lens, out=out)
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
+        _require(t.dtype == torch.bfloat16, f"{name} must be bfloat16")
+    _require(out.shape == q.shape, "out must have q's shape")
+    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+             "block_table and seq_lens must be int32")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape, "k_pool/v_pool: [P, ps, Hkv, d]")
+    _require(q.dim() == 3 and q.shape[2] == k_pool.shape[3], "q: [batch, Hq, d]")
+    _require(seq_lens.numel() == q.shape[0] and block_table.shape[0] >= q.shape[0],
+             "seq_lens: [batch]; block_table: [batch, maxp]")
+    lay = layout_of(k_pool, block_table)
+    _check(load_library().pa_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), float(scale),
+        _ptr(out), q.shape[0], q.shape[1], ctypes.byref(lay), _stream(stream)))
     return out
 
 

@@ -113,7 +113,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
                         const int32_t* block_table, const int32_t* seq_lens, float scale,
                         int32_t batch, int32_t num_q_heads, const void* workspace,
-                        size_t workspace_bytes, const pa_kv_layout* layout, bool need_inputs) {
+                        size_t workspace_bytes, const pa_kv_layout* layout, bool need_inputs,
+                        bool check_workspace = true) {
   int st = check_layout(layout, num_q_heads);
   if (st) return st;
   if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch=%d must be >= 0", batch);
@@ -130,6 +131,7 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
   if (max_splits_of(layout, num_q_heads) > 65535)
     return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size = %lld needs more than 65535 "
                 "decode splits", (long long)layout->max_pages_per_seq * layout->page_size);
+  if (!check_workspace) return PA_OK;
   const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (!aligned16(workspace))
@@ -298,6 +300,31 @@ int pa_decode(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
               const pa_kv_layout* layout, hipStream_t stream) {
   return pa_decode_window(q, k_pool, v_pool, block_table, seq_lens, scale, out, batch,
                           num_q_heads, 0, workspace, workspace_bytes, layout, stream);
+}
+
+int pa_decode_noalloc(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, float scale,
+                      pa_bf16* out, int32_t batch, int32_t num_q_heads,
+                      const pa_kv_layout* layout, hipStream_t stream) {
+  // every argument is checked before any HIP call, so a refused call touches no device
+  int st = check_decode_common(q, k_pool, v_pool, block_table, seq_lens, scale, batch,
+                               num_q_heads, nullptr, 0, layout, true, false);
+  if (st) return st;
+  if (!out) return fail(PA_ERR_NULL, "out must be non-NULL");
+  const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
+  if (need > PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode_noalloc: %d sequences x %d query heads over up to %lld tokens need "
+                "%zu bytes of partials, above the library's static %zu-byte workspace; use "
+                "pa_decode with a caller workspace",
+                batch, num_q_heads, (long long)layout->max_pages_per_seq * layout->page_size,
+                need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  if (batch == 0) return ok();
+  void* scratch = nullptr;
+  st = hip_status(pa::static_decode_workspace(&scratch), "static decode workspace lookup");
+  if (st) return st;
+  return pa_decode_window(q, k_pool, v_pool, block_table, seq_lens, scale, out, batch,
+                          num_q_heads, 0, scratch, PA_NOALLOC_SCRATCH_BYTES, layout, stream);
 }
 
 int pa_kv_append(const pa_bf16* k_new, const pa_bf16* v_new, const int32_t* seq_ids,

@@ -104,6 +104,9 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial_gqa(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+// Device address of the current GPU's static decode workspace (PA_NOALLOC_SCRATCH_BYTES
+// bytes), looked up on the first call per device and kept.
+hipError_t static_decode_workspace(void** ptr);
 hipError_t launch_copy_pages(const CopyPagesArgs& a, hipStream_t stream);
 
 }  // namespace pa

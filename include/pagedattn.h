@@ -192,6 +192,36 @@ int pa_decode_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_p
                      hipStream_t stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same result, bit for bit, with the split
+ * partials kept in a workspace that lives inside the library itself, a static
+ * device array of PA_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the first
+ * call on that GPU until the process ends.  The call allocates nothing, frees
+ * nothing and synchronises nothing; its first call on a device looks the array's
+ * address up once (hipGetSymbolAddress) with that device current.
+ *
+ *   arguments  as for pa_decode, without the workspace; the stream must belong
+ *              to the current device
+ *   limit      pa_decode_workspace_bytes(batch, num_q_heads, layout) must not
+ *              exceed PA_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. 64 sequences x 32
+ *              heads x 8192 tokens, d = 128); larger requests fail with
+ *              PA_ERR_WORKSPACE and enqueue nothing (use pa_decode)
+ *   sharing    every call on a GPU uses that GPU's one array: calls whose work
+ *              overlaps on one GPU (other streams, other threads) race and give
+ *              undefined results; calls ordered on one stream are safe.  The
+ *              array keeps the last call's partials; nothing in it needs to start
+ *              at zero (each call writes every partial it later reads).
+ * Errors: those of pa_decode; PA_ERR_WORKSPACE (request above the limit);
+ * PA_ERR_HIP (no current device, or the array's address lookup failed).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_decode_noalloc(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, float scale,
+                      pa_bf16* out, int32_t batch, int32_t num_q_heads,
+                      const pa_kv_layout* layout, hipStream_t stream);
+
+/*
  * pa_kv_append -- write the K and V rows of new tokens into their pages, the step
  * before attention in autoregressive decoding ([FA-LLM] "KV Cache": the new K_t,
  * V_t join the cache, then the token attends over it).  Token i of sequence

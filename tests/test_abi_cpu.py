@@ -157,6 +157,39 @@ def test_decode_rejects(lib):
     assert st == B.PA_ERR_NULL
 
 
+def test_decode_noalloc_rejects_before_any_hip_call(lib):
+    """The no-allocation decode checks every argument, and the size of the partials
+    against its static workspace, before it looks the workspace up on a device."""
+    layout = B.make_layout(100, 16, 4, 128, 10)
+    call = lambda **kw: lib.pa_decode_noalloc(
+        kw.get("q", FAKE), FAKE, FAKE, FAKE, kw.get("lens", FAKE), kw.get("scale", 0.1),
+        kw.get("out", FAKE), kw.get("batch", 2), kw.get("hq", 4),
+        ctypes.byref(kw.get("layout", layout)), None)
+    assert call(q=None) == B.PA_ERR_NULL
+    assert call(out=None) == B.PA_ERR_NULL
+    assert call(lens=None) == B.PA_ERR_NULL
+    assert call(scale=-1.0) == B.PA_ERR_INVALID_ARG
+    assert call(hq=6) == B.PA_ERR_INVALID_ARG
+    assert call(batch=-1) == B.PA_ERR_INVALID_ARG
+    assert call(layout=B.make_layout(100, 16, 4, 80, 10)) == B.PA_ERR_UNSUPPORTED
+    # 128 sequences x 32 heads over up to 32768 tokens: 272 MB of partials > 64 MiB
+    mixed = B.make_layout(70000, 16, 32, 128, 2048)
+    need = lib.pa_decode_workspace_bytes(128, 32, ctypes.byref(mixed))
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    assert call(layout=mixed, batch=128, hq=32) == B.PA_ERR_WORKSPACE
+    assert "static" in B.last_error() and str(B.NOALLOC_SCRATCH_BYTES) in B.last_error()
+    # the 64-sequence decode batch (32 heads, up to 8192 tokens) fits
+    dec = B.make_layout(20000, 16, 32, 128, 512)
+    assert lib.pa_decode_workspace_bytes(64, 32, ctypes.byref(dec)) <= B.NOALLOC_SCRATCH_BYTES
+    assert call(batch=0) == B.PA_OK
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    assert "#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert B.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(4, 1, 64, dtype=torch.bfloat16)

@@ -1,15 +1,34 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
-Default workload: decode_64 (64 sequences x 1 query token, 32 heads, d=128,
-lengths uniform on {512..8192}, 16-token pages in a shuffled pool).  One step is
-one pa_decode over the batch (the split pass and the combine pass, issued as
-pa_decode_partial + pa_decode_combine so each kernel can be timed with HIP events
-on the stream it runs on).  `value` is algorithmic KV bytes per second over whole
-steps; `roofline` rates the split kernel alone against 8 TB/s.  A `prefill` object
-times the causal N=4096 prefill (32 heads, d=128) against the 2.5 PFLOP/s dense
-bf16 MFMA peak.  `cpu_baseline` times the CPU oracle on a bounded sample.
+Every workload of the set runs in the default invocation, each on seeded synthetic
+inputs already resident in device memory, each kernel launch bracketed by HIP events
+on the stream the library launches on (torch's current stream):
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  decode_64               64 sequences x 1 query token, 32 heads, d=128, lengths
+                          uniform on {512..8192}, 16-token pages in a shuffled pool.
+                          One step = pa_decode_partial + pa_decode_combine.  `value`
+                          is its KV bytes per second over whole steps (the headline);
+                          `roofline` rates the split kernel alone against 8 TB/s.
+  prefill_4096_causal     N=4096, 32 heads, d=128, identity table     -> `prefill`
+  prefill_4096_noncausal  the same, non-causal                         -> `prefill_noncausal`
+  prefill_32k             causal N=32768, 8 heads, shuffled pages of 256 -> `prefill_long`
+  mixed_128x4             128 lognormal decode sequences + 4 causal 2048-row chunks
+                          on 8192 cached tokens, one pool -> `mixed` (decode GB/s,
+                          chunk TFLOP/s, combined T_roof / T_meas)
+  prefill_600             the worked example's layout (600 tokens, table [5, 1, 9],
+                          d=64): launch-latency bound, reported in microseconds
+  next                    the rows beyond the core path (grouped heads, KV append,
+                          page copy, sliding windows)             -> `next_rows`
+
+Each kernel's rate uses its average event-timed launch (the figure rocprofv3's
+average duration is compared with); median and minimum are reported beside it.
+`input_sha256` holds a digest of every input buffer of every workload.
+`cpu_baseline` times the CPU oracle over a pool of host processes on decode_64 and on
+query rows of the two causal prefills, and compares the oracle's outputs with the
+GPU outputs of the timed runs (`parity`).
+
+Usage: python bench.py [--steps K] [--warmup W] [--legs a,b,...] [--no-cpu-baseline]
+       [--no-digest]
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
@@ -147,11 +166,24 @@ def decode_kernel_name(wl) -> str:
     return f"{KERNEL_FILES[decode_kind(wl)]}<{wl.head_dim}>"
 
 
-def timed_decode(wl, call, steps, warmup):
+def timing_stats(ms):
+    """avg / median / min of a list of HIP-event durations (ms)."""
+    s = sorted(ms)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    return {"avg": sum(s) / n, "median": med, "min": s[0]}
+
+
+def _ms(st, key):
+    return round(st[key], 4)
+
+
+def timed_decode(wl, call, out, steps, warmup):
+    """K decode steps (pass 1 + combine, each bracketed by HIP events on torch's current
+    stream, the stream the library launches on); returns (wall s, pass-1 ms, combine ms)."""
     import torch
     from exact_tiled_attention_pa_amd import binding as B
     ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
-    out = torch.empty_like(call.q)
     lay = B.layout_of(wl.k_pool, call.block_table)
 
     def step():
@@ -173,55 +205,94 @@ def timed_decode(wl, call, steps, warmup):
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    return wall, split_ms, comb_ms
+    return wall, [e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev]
 
 
-def timed_prefill(wl, call, steps, warmup):
+def timed_launches(fn, steps, warmup):
+    """(wall s, HIP-event durations in ms) of `steps` launches of fn on torch's current
+    stream, after `warmup` untimed ones."""
     import torch
-    from exact_tiled_attention_pa_amd import binding as B
-    out = torch.empty_like(call.q)
-
-    def run():
-        B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
-                     call.causal, wl.scale, out, call.q_start, call.max_q_len)
-
     for _ in range(warmup):
-        run()
+        fn()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        run()
+        fn()
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, [e[0].elapsed_time(e[1]) for e in ev]
 
 
-def timed_launches(fn, steps, warmup):
-    """HIP-event durations (ms) of `steps` launches of fn on torch's current stream."""
-    import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        fn()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    return [e[0].elapsed_time(e[1]) for e in ev]
-
-
-def _rate(nbytes_or_flops, ms, peak, unit, **extra):
-    avg = sum(ms) / len(ms)
+def _rate(work, ms, peak, unit, **extra):
+    """Rate of one kernel against its peak from the average event-timed launch, with the
+    median and minimum beside it."""
+    st = timing_stats(ms)
     scale = 1e9 if unit == "GB/s" else 1e12
-    achieved = nbytes_or_flops / (avg * 1e-3) / scale
+    achieved = work / (st["avg"] * 1e-3) / scale
     return dict(extra, achieved=round(achieved, 2), unit=unit, peak=peak,
-                frac=round(achieved / peak, 4), kernel_ms_avg=round(avg, 4))
+                frac=round(achieved / peak, 4), kernel_ms_avg=_ms(st, "avg"),
+                kernel_ms_median=_ms(st, "median"), kernel_ms_min=_ms(st, "min"))
+
+
+def decode_leg(wl, call, steps, warmup):
+    """decode: KV bytes per second over whole steps, and pass 1 against 8 TB/s."""
+    import torch
+    nbytes = decode_kv_bytes(wl, call)
+    out = torch.empty_like(call.q)
+    wall, split_ms, comb_ms = timed_decode(wl, call, out, steps, warmup)
+    ms_step = wall / steps * 1e3
+    roof = _rate(nbytes, split_ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+                 kernel=decode_kernel_name(wl))
+    cst = timing_stats(comb_ms)
+    roof.update(traffic=recorded_traffic(decode_kind(wl), wl.name),
+                combine_ms_avg=_ms(cst, "avg"), combine_ms_median=_ms(cst, "median"))
+    res = {"workload": wl.name, "gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+           "ms_per_step": round(ms_step, 4), "kv_bytes_per_step": nbytes,
+           "total_tokens": int(call.seq_lens_host.sum()), "roofline": roof}
+    return res, out
+
+
+def prefill_leg(wl, call, steps, warmup):
+    """prefill: FLOPs of the visible pairs against 2.5 PFLOP/s, per launch."""
+    import torch
+    from exact_tiled_attention_pa_amd import binding as B
+    flops, nbytes = prefill_work(wl, call)
+    out = torch.empty_like(call.q)
+
+    def run():
+        B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
+                     call.causal, wl.scale, out, call.q_start, call.max_q_len)
+
+    wall, ms = timed_launches(run, steps, warmup)
+    roof = _rate(flops, ms, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
+                 kernel=f"prefill_kernel<{wl.head_dim}, {str(call.causal).lower()}>")
+    wl_key = wl.name if len(wl.calls) == 1 else f"{wl.name}_chunks"
+    roof.update(traffic=recorded_traffic("prefill", wl_key),
+                mfma_busy=recorded_mfma("prefill", wl_key))
+    res = {"workload": wl.name, "causal": call.causal, "tflops": roof["achieved"],
+           "kernel_ms_avg": roof["kernel_ms_avg"], "kernel_ms_median": roof["kernel_ms_median"],
+           "kernel_ms_min": roof["kernel_ms_min"],
+           "us_per_call_wall": round(wall / steps * 1e6, 2), "flops_per_launch": flops,
+           "alg_bytes_per_launch": nbytes, "roofline": roof}
+    return res, out
+
+
+def mixed_leg(wl, steps, warmup):
+    """mixed batch: the decode call and the chunk prefill over one pool, each timed, and
+    the combined fraction T_roof / T_meas with T_roof = bytes / 8 TB/s + FLOPs / 2.5 PF."""
+    dec, dec_out = decode_leg(wl, wl.calls[0], steps, warmup)
+    chunks, pre_out = prefill_leg(wl, wl.calls[1], steps, warmup)
+    t_roof = dec["kv_bytes_per_step"] / (HBM_PEAK_GBS * 1e9) + chunks["flops_per_launch"] / (
+        MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_meas = (dec["roofline"]["kernel_ms_avg"] + dec["roofline"]["combine_ms_avg"] +
+              chunks["kernel_ms_avg"]) * 1e-3
+    res = {"workload": wl.name, "decode": dec, "chunks": chunks,
+           "combined_roofline_fraction": round(t_roof / t_meas, 4),
+           "combined_ms": round(t_meas * 1e3, 4)}
+    return res, (dec_out, pre_out)
 
 
 def next_rows_summary(decode_wl, steps, warmup):
@@ -238,9 +309,10 @@ def next_rows_summary(decode_wl, steps, warmup):
     ws = B.decode_workspace(call.q, decode_wl.k_pool, call.block_table)
     out = torch.empty_like(call.q)
     w = 1024
-    ms = timed_launches(lambda: B.pa_decode(call.q, decode_wl.k_pool, decode_wl.v_pool,
-                                            call.block_table, call.seq_lens, decode_wl.scale,
-                                            out, ws, window=w), steps, warmup)
+    _, ms = timed_launches(lambda: B.pa_decode(call.q, decode_wl.k_pool, decode_wl.v_pool,
+                                               call.block_table, call.seq_lens,
+                                               decode_wl.scale, out, ws, window=w),
+                           steps, warmup)
     seen = np.minimum(call.seq_lens_host.astype(np.int64), w).sum()
     nbytes = int(seen) * 2 * decode_wl.heads * decode_wl.head_dim * 2
     res["window_decode"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
@@ -252,12 +324,13 @@ def next_rows_summary(decode_wl, steps, warmup):
     g = W.decode_64_gqa8(device="cuda")
     gc = g.calls[0]
     ws = B.decode_workspace(gc.q, g.k_pool, gc.block_table)
-    out = torch.empty_like(gc.q)
-    ms = timed_launches(lambda: B.pa_decode_partial(gc.q, g.k_pool, g.v_pool, gc.block_table,
-                                                    gc.seq_lens, g.scale, ws), steps, warmup)
+    _, ms = timed_launches(lambda: B.pa_decode_partial(gc.q, g.k_pool, g.v_pool,
+                                                       gc.block_table, gc.seq_lens, g.scale,
+                                                       ws), steps, warmup)
     res["gqa_decode"] = _rate(decode_kv_bytes(g, gc), ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
-                              workload=g.name, kernel=decode_kernel_name(g))
-    del g, gc, ws, out
+                              workload=g.name, kernel=decode_kernel_name(g),
+                              traffic=recorded_traffic("decode_gqa", g.name))
+    del g, gc, ws
 
     # f2: appending a 4096-token chunk of one sequence (32 K/V heads, d=128, pages of 16)
     n_tok, heads, d, ps = 4096, 32, 128, 16
@@ -268,13 +341,12 @@ def next_rows_summary(decode_wl, steps, warmup):
     v_new = W.normal_bf16((n_tok, heads, d), 1.0, 13, "cuda")
     ids = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
     pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
-    ms = timed_launches(lambda: B.pa_kv_append(k_new, v_new, ids, pos, a.k_pool, a.v_pool,
-                                               ac.block_table), steps, warmup)
+    _, ms = timed_launches(lambda: B.pa_kv_append(k_new, v_new, ids, pos, a.k_pool, a.v_pool,
+                                                  ac.block_table), steps, warmup)
     nbytes = n_tok * heads * d * 2 * 2 * 2  # K and V rows, read once and written once
     res["kv_append"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
                              workload="append_4096: 4096 tokens, 32 K/V heads, d=128, "
                                       "pages of 16, shuffled", kernel="kv_append_kernel")
-
     del a, ac, k_new, v_new, ids, pos
 
     # f3: copy-on-write page copies: 2048 disjoint page pairs in a 4096-page pool
@@ -284,7 +356,7 @@ def next_rows_summary(decode_wl, steps, warmup):
     perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(16))
     src = perm[:n_pairs].to(torch.int32).cuda()
     dst = perm[n_pairs:2 * n_pairs].to(torch.int32).cuda()
-    ms = timed_launches(lambda: B.pa_copy_pages(kp, vp, src, dst), steps, warmup)
+    _, ms = timed_launches(lambda: B.pa_copy_pages(kp, vp, src, dst), steps, warmup)
     page_bytes = ps * heads * d * 2
     nbytes = n_pairs * page_bytes * 2 * 2  # both pools, read and write
     res["copy_pages"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
@@ -297,121 +369,193 @@ def next_rows_summary(decode_wl, steps, warmup):
     pc = p.calls[0]
     out = torch.empty_like(pc.q)
     w = 4096
-    ms = timed_launches(lambda: B.pa_prefill(pc.q, p.k_pool, p.v_pool, pc.block_table,
-                                             pc.seq_lens, True, p.scale, out, pc.q_start,
-                                             pc.max_q_len, window=w), steps, warmup)
+    _, ms = timed_launches(lambda: B.pa_prefill(pc.q, p.k_pool, p.v_pool, pc.block_table,
+                                                pc.seq_lens, True, p.scale, out, pc.q_start,
+                                                pc.max_q_len, window=w), steps, warmup)
     n = int(pc.seq_lens_host[0])
     pairs = w * (w + 1) // 2 + (n - w) * w
     flops = 4 * p.head_dim * pc.q.shape[1] * pairs
     res["window_prefill"] = _rate(flops, ms, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
-                                  workload=f"prefill_32k, window {w}", kernel="prefill_kernel")
+                                  workload=f"prefill_32k, window {w}",
+                                  kernel="prefill_kernel<128, true>")
     del p, pc, out
     torch.cuda.empty_cache()
     return res
 
 
-def prefill_summary(wl, call, steps, warmup):
-    flops, nbytes = prefill_work(wl, call)
-    wall, ms = timed_prefill(wl, call, steps, warmup)
-    avg = sum(ms) / len(ms)
-    tflops = flops / (avg * 1e-3) / 1e12
-    traffic = recorded_traffic("prefill", wl.name)
-    mfma_busy = recorded_mfma("prefill", wl.name) if call.causal else None
-    return {
-        "workload": wl.name,
-        "tflops": round(tflops, 2),
-        "kernel_ms_avg": round(avg, 4),
-        "kernel_ms_min": round(min(ms), 4),
-        "ms_per_call_wall": round(wall / steps * 1e3, 4),
-        "flops_per_launch": flops,
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "mfma_busy": mfma_busy},
-        "alg_bytes_per_launch": nbytes,
-    }
+# ------------------------------------------------------------------ CPU baseline (oracle)
+#
+# The oracle as it stands (NumPy fp64, oracle/attention.py), never tuned for speed, run
+# over a process pool of the host's cores (one BLAS thread per process) on whole decode
+# sequences or on query rows of a prefill.  Inputs are the same host bit patterns the GPU
+# legs ran on, written once to files the workers memory-map.  The oracle's outputs for the
+# evaluated rows are also compared with the GPU outputs of the timed runs.
+
+_WORKER_CACHE = {}
+_BLAS_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
 
 
-# ------------------------------------------------------------------ CPU baseline
-
-def cpu_baseline_decode(wl, call, budget_s=10.0):
-    """The oracle as it stands, single BLAS thread, on whole sequences of the same
-    batch, in order and wrapping around, until about budget_s seconds of CPU work;
-    reported in GB/s of KV read.  Host copies of the pages are not timed."""
-    import numpy as np
-    import torch
+def _worker_init(_=None):
     from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def _worker_arrays(paths):
+    import numpy as np
+    key = tuple(paths)
+    if key not in _WORKER_CACHE:
+        _WORKER_CACHE.clear()
+        _WORKER_CACHE[key] = [np.load(p, mmap_mode="r") for p in paths]
+    return _WORKER_CACHE[key]
+
+
+def _oracle_task(task):
+    """One unit of oracle work in a pool worker: decode of some sequences, or some query
+    rows of one prefill sequence.  Returns (outputs of those rows, seconds spent)."""
+    from oracle import attention as OA
+    kind, paths, meta, sel = task
+    q, k, v, table, lens = _worker_arrays(paths)[:5]
+    t0 = time.perf_counter()
+    if kind == "decode":
+        out, _ = OA.paged_decode(q, k, v, table, lens, meta["scale"], seqs=sel)
+        res = out[sel]
+    else:
+        q_start = _worker_arrays(paths)[5]
+        b = meta["seq"]
+        out, _ = OA.paged_prefill(q, k, v, table, lens, q_start, meta["causal"], meta["scale"],
+                                  rows={b: sel})
+        res = out[int(q_start[b]) + sel]
+    return res, time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_workers() -> int:
+    """Processes for the oracle pool: the host cores this process may run on, at most 16
+    (the host share of one GPU on the measurement machines)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _parity(got_bits, ref):
+    """max / mean |O_gpu - O_ref| and the largest per-(row, head) max error divided by
+    that row's RMS(O_ref), over the rows the oracle evaluated."""
+    import numpy as np
+    from oracle import attention as OA
+    got = OA.bf16_to_f64(got_bits)
+    err = np.abs(got - ref)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1))
+    ratio = err.max(axis=-1) / np.maximum(rms, 1e-300)
+    return {"elements": int(err.size), "max_abs": float(f"{err.max():.4e}"),
+            "mean_abs": float(f"{err.mean():.4e}"),
+            "max_err_over_rms_ref": float(f"{ratio.max():.4e}"),
+            "within_tolerance": bool(err.max() <= 1e-2 and err.mean() <= 1e-3)}
+
+
+def cpu_baseline(legs, scratch_dir):
+    """Times the oracle over a process pool on each leg's sample; returns the baseline
+    record (headline: decode GB/s) with one entry per leg, each with parity figures."""
+    import multiprocessing as mp
+
+    import numpy as np
 
     from exact_tiled_attention_pa_amd import workloads as W
-    from oracle import attention as OA
 
-    q = W.to_host_bits(call.q)
-    done_bytes = 0
-    done_tokens = 0
-    spent = 0.0
-    count = 0
-    with threadpool_limits(limits=1):
-        while spent < budget_s:
-            b = count % call.batch
-            L = int(call.seq_lens_host[b])
-            n = -(-L // wl.page_size)
-            pages = call.block_table_host[b, :n]
-            sel = torch.as_tensor(pages.astype("int64"), device=wl.k_pool.device)
-            k = W.to_host_bits(wl.k_pool.index_select(0, sel))
-            v = W.to_host_bits(wl.v_pool.index_select(0, sel))
-            table = np.arange(n, dtype=np.int64)[None, :]
+    n = cpu_workers()
+    ctx = mp.get_context("spawn")
+    entries = {}
+    total = 0.0
+    # one BLAS thread per worker process, fixed before the workers import NumPy
+    saved = {k: os.environ.get(k) for k in _BLAS_THREAD_VARS}
+    os.environ.update({k: "1" for k in _BLAS_THREAD_VARS})
+    try:
+        pool = ctx.Pool(n, initializer=_worker_init)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    with pool:
+        pool.map(_worker_init, range(n))  # workers up and imported before any timing
+        for name, (wl, call, out, sample) in legs.items():
+            base = os.path.join(scratch_dir, name)
+            arrays = [W.to_host_bits(call.q), W.to_host_bits(wl.k_pool),
+                      W.to_host_bits(wl.v_pool), call.block_table_host.astype(np.int64),
+                      call.seq_lens_host.astype(np.int64)]
+            if call.kind == "prefill":
+                arrays.append(call.q_start_host.astype(np.int64))
+            paths = []
+            for i, a in enumerate(arrays):
+                p = f"{base}_{i}.npy"
+                np.save(p, a)
+                paths.append(p)
+            del arrays
+            meta = {"scale": wl.scale, "causal": call.causal, "seq": 0}
+            if call.kind == "decode":
+                tasks = [("decode", paths, meta, [int(b)]) for b in sample]
+            else:
+                tasks = [("prefill", paths, meta, rows) for rows in sample]
             t0 = time.perf_counter()
-            OA.paged_decode(q[b:b + 1], k, v, table, call.seq_lens_host[b:b + 1], wl.scale)
-            spent += time.perf_counter() - t0
-            done_bytes += L * 2 * wl.heads * wl.head_dim * 2
-            done_tokens += L
-            count += 1
-    return {
-        "value": round(done_bytes / spent / 1e9, 4),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"oracle (NumPy fp64, 1 BLAS thread) on {count} decode sequences of the "
-                  f"{call.batch}-sequence batch taken in order ({done_tokens} tokens, all "
-                  f"{wl.num_q_heads} query heads) in {spent:.1f} s",
-    }
+            results = pool.map(_oracle_task, tasks, chunksize=1)
+            wall = time.perf_counter() - t0
+            total += wall
+            got = W.to_host_bits(out)
+            if call.kind == "decode":
+                ref = np.concatenate([r for r, _ in results])
+                rows_bits = got[np.asarray(sample)]
+                work = sum(int(call.seq_lens_host[b]) for b in sample) * 2 * wl.heads * \
+                    wl.head_dim * 2
+                rate, unit = work / wall / 1e9, "GB/s"
+                what = (f"{len(sample)} whole decode sequences ({sum(int(call.seq_lens_host[b]) for b in sample)} "
+                        f"tokens, all {wl.num_q_heads} query heads)")
+            else:
+                ref = np.concatenate([r for r, _ in results])
+                rows = np.concatenate(sample)
+                rows_bits = got[int(call.q_start_host[0]) + rows]
+                L, q_len = int(call.seq_lens_host[0]), int(call.q_start_host[1])
+                pos = L - q_len + rows
+                pairs = int(np.minimum(pos + 1, L).sum()) if call.causal else L * len(rows)
+                work = 4 * wl.head_dim * wl.num_q_heads * pairs
+                rate, unit = work / wall / 1e12, "TFLOP/s"
+                what = (f"{len(rows)} of {q_len} query rows spread over the sequence, all "
+                        f"{wl.num_q_heads} heads ({pairs} visible pairs per head)")
+            entries[name] = {"value": round(rate, 6), "unit": unit, "wall_s": round(wall, 2),
+                             "cpu_s": round(sum(t for _, t in results), 2), "sample": what,
+                             "parity": _parity(rows_bits, ref)}
+            for p in paths:
+                os.remove(p)
+            _WORKER_CACHE.clear()
+            log(f"cpu baseline {name}: {rate:.4g} {unit} in {wall:.1f} s, "
+                f"parity {entries[name]['parity']}")
+    head = entries.get("decode_64") or next(iter(entries.values()))
+    return {"value": head["value"], "unit": head["unit"], "cores": n, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"oracle (NumPy fp64, one BLAS thread per process, {n} processes) on "
+                      f"{head['sample']}; {total:.1f} s wall over all legs",
+            "legs": entries}
 
 
-def cpu_baseline_prefill(wl, call, budget_s=15.0):
-    """Oracle on query rows of the first sequence, spread over the whole range."""
+def baseline_samples(name, wl, call):
+    """What the oracle evaluates for each leg: whole decode sequences, or query rows
+    (every row-stride-th row, from an offset) split into tasks."""
     import numpy as np
-    import torch
-    from threadpoolctl import threadpool_limits
-
-    from exact_tiled_attention_pa_amd import workloads as W
-    from oracle import attention as OA
-
-    q = W.to_host_bits(call.q)
-    k = W.to_host_bits(wl.k_pool)
-    v = W.to_host_bits(wl.v_pool)
-    q_len = int(call.q_start_host[1] - call.q_start_host[0])
-    L = int(call.seq_lens_host[0])
-    n_rows, spent, pairs = 16, 0.0, 0
-    with threadpool_limits(limits=1):
-        while spent < budget_s and n_rows <= q_len:
-            rows = np.linspace(0, q_len - 1, n_rows).astype(np.int64)
-            t0 = time.perf_counter()
-            OA.paged_prefill(q, k, v, call.block_table_host, call.seq_lens_host,
-                             call.q_start_host, call.causal, wl.scale, rows={0: rows})
-            spent = time.perf_counter() - t0
-            pos = L - q_len + rows
-            pairs = int((pos + 1).sum()) if call.causal else L * len(rows)
-            n_rows *= 2
-    hq = call.q.shape[1]
-    flops = 4 * wl.head_dim * hq * pairs
-    return {
-        "value": round(flops / spent / 1e12, 6),
-        "unit": "TFLOP/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"oracle (NumPy fp64, 1 BLAS thread) on {n_rows // 2} query rows of "
-                  f"{q_len}, all {hq} heads, in {spent:.1f} s",
-    }
+    if call.kind == "decode":
+        return list(range(call.batch))
+    q_len = int(call.q_start_host[1])
+    stride = {"prefill_32k": 8}.get(name, 1)
+    rows = np.arange(stride // 2, q_len, stride, dtype=np.int64)
+    per_task = 32
+    return [rows[i:i + per_task] for i in range(0, len(rows), per_task)]
 
 
 # ------------------------------------------------------------------ rocprofv3 summaries
@@ -520,22 +664,21 @@ def summarize_mfma(pmc_dir, kind, workload, out_path, command):
 
 # ------------------------------------------------------------------ main
 
+LEGS = ("decode_64", "prefill_4096_causal", "prefill_4096_noncausal", "prefill_32k",
+        "mixed_128x4", "prefill_600", "next")
+BASELINE_LEGS = ("decode_64", "prefill_4096_causal", "prefill_32k")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode_64")
-    ap.add_argument("--prefill-workload", default="prefill_4096_causal")
-    ap.add_argument("--prefill-long-workload", default="prefill_32k",
-                    help="second prefill leg: the long causal context")
-    ap.add_argument("--no-prefill-long", action="store_true")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated legs to run (default: all): " + ", ".join(LEGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-next", action="store_true",
-                    help="skip the grouped-head / append / copy / window legs")
-    ap.add_argument("--only-next", action="store_true",
-                    help="run only those legs (on the decode_64 batch) and print them")
+    ap.add_argument("--no-digest", action="store_true",
+                    help="skip the SHA-256 of every input buffer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
@@ -563,6 +706,10 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
+    legs = [x for x in args.legs.split(",") if x]
+    unknown = [x for x in legs if x not in LEGS]
+    if unknown:
+        raise SystemExit(f"unknown legs {unknown}; choose from {LEGS}")
 
     import torch
     from exact_tiled_attention_pa_amd import binding as B
@@ -583,95 +730,81 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.only_next:
-        wl = W.decode_64(device="cuda")
-        print(json.dumps({"next_rows": next_rows_summary(wl, args.steps, args.warmup)}),
-              flush=True)
-        return
-
-    if args.workload not in W.FULL_WORKLOADS:
-        raise SystemExit(f"unknown workload {args.workload}")
-    log(f"generating {args.workload}")
-    wl = W.FULL_WORKLOADS[args.workload](device="cuda")
-    torch.cuda.synchronize()
-
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic"}
-    call = wl.calls[0]
-    if call.kind == "decode":
-        nbytes = decode_kv_bytes(wl, call)
-        log(f"decode: {call.batch} seqs, {int(call.seq_lens_host.sum())} tokens, "
-            f"{nbytes / 1e9:.3f} GB of K/V per step")
-        wall, split_ms, comb_ms = timed_decode(wl, call, args.steps, args.warmup)
-        ms_step = wall / args.steps * 1e3
-        split_avg = sum(split_ms) / len(split_ms)
-        achieved = nbytes / (split_avg * 1e-3) / 1e9
-        traffic = recorded_traffic(decode_kind(wl), wl.name)
-        result.update({
-            "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
-            "unit": "GB/s",
-            "ms_per_step": round(ms_step, 4),
-            "config": {"workload": wl.name, "batch": call.batch, "heads": wl.num_q_heads,
-                       "kv_heads": wl.heads, "head_dim": wl.head_dim,
-                       "page_size": wl.page_size,
-                       "total_tokens": int(call.seq_lens_host.sum()),
-                       "kv_bytes_per_step": nbytes, "description": wl.description},
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                         "kernel": decode_kernel_name(wl),
-                         "kernel_ms_avg": round(split_avg, 4),
-                         "combine_ms_avg": round(sum(comb_ms) / len(comb_ms), 4)},
-        })
-        if len(wl.calls) > 1:  # mixed batch: the prefill chunks on the same pools
-            chunks = wl.calls[1]
-            cs = prefill_summary(wl, chunks, args.steps, args.warmup)
-            t_roof = nbytes / (HBM_PEAK_GBS * 1e9) + cs["flops_per_launch"] / (
-                MFMA_BF16_PEAK_TFLOPS * 1e12)
-            t_meas = (split_avg + sum(comb_ms) / len(comb_ms) + cs["kernel_ms_avg"]) * 1e-3
-            result["chunks"] = cs
-            result["combined_roofline_fraction"] = round(t_roof / t_meas, 4)
-    else:
-        s = prefill_summary(wl, call, args.steps, args.warmup)
-        result.update({
-            "value": s["tflops"], "unit": "TFLOP/s", "ms_per_step": s["ms_per_call_wall"],
-            "config": {"workload": wl.name, "heads": wl.heads, "head_dim": wl.head_dim,
-                       "page_size": wl.page_size, "causal": call.causal,
-                       "description": wl.description},
-            "roofline": dict(s["roofline"], kernel="prefill_kernel",
-                             kernel_ms_avg=s["kernel_ms_avg"]),
-        })
+    kept = {}      # leg -> (workload, call, GPU output) for the digests and the baseline
+    workloads = {}
+    # the headline legs run first: the clock the chip holds depends on how long it has
+    # been loaded, and the prefill legs warm up for at least 10 launches
+    for leg in legs:
+        if leg == "next":
+            continue
+        log(f"leg {leg}: generating inputs")
+        wl = W.FULL_WORKLOADS[leg](device="cuda")
+        torch.cuda.synchronize()
+        workloads[leg] = wl
+        if leg == "decode_64":
+            res, out = decode_leg(wl, wl.calls[0], args.steps, args.warmup)
+            kept[leg] = (wl, wl.calls[0], out)
+            result.update({
+                "value": res["gbs"], "unit": "GB/s", "ms_per_step": res["ms_per_step"],
+                "config": {"workload": wl.name, "batch": wl.calls[0].batch,
+                           "heads": wl.num_q_heads, "kv_heads": wl.heads,
+                           "head_dim": wl.head_dim, "page_size": wl.page_size,
+                           "total_tokens": res["total_tokens"],
+                           "kv_bytes_per_step": res["kv_bytes_per_step"],
+                           "description": wl.description},
+                "roofline": res["roofline"],
+            })
+        elif leg == "mixed_128x4":
+            res, (dout, pout) = mixed_leg(wl, args.steps, max(args.warmup, 10))
+            kept[leg] = (wl, wl.calls[1], pout)
+            result["mixed"] = res
+        else:
+            res, out = prefill_leg(wl, wl.calls[0], args.steps,
+                                   max(args.warmup, 3 if leg == "prefill_32k" else 10))
+            kept[leg] = (wl, wl.calls[0], out)
+            key = {"prefill_4096_causal": "prefill", "prefill_4096_noncausal": "prefill_noncausal",
+                   "prefill_32k": "prefill_long", "prefill_600": "prefill_600"}[leg]
+            result[key] = res
+        log(f"leg {leg}: done")
+    if "value" not in result:  # no decode leg: the first leg's rate heads the line
+        first = next(k for k in ("prefill", "prefill_noncausal", "prefill_long", "prefill_600")
+                     if k in result)
+        s = result[first]
+        result.update({"value": s["tflops"], "unit": "TFLOP/s",
+                       "ms_per_step": round(s["us_per_call_wall"] / 1e3, 4),
+                       "config": {"workload": s["workload"], "causal": s["causal"]},
+                       "roofline": s["roofline"]})
 
-    if not args.no_prefill and call.kind == "decode":
-        log(f"prefill leg: {args.prefill_workload}")
-        pw = W.FULL_WORKLOADS[args.prefill_workload](device="cuda")
-        # a longer warm-up: the leg follows the decode loop and must not time clock ramps
-        result["prefill"] = prefill_summary(pw, pw.calls[0], args.steps, max(args.warmup, 10))
-        del pw
-        if not args.no_prefill_long:
-            log(f"prefill leg: {args.prefill_long_workload}")
-            pw = W.FULL_WORKLOADS[args.prefill_long_workload](device="cuda")
-            result["prefill_long"] = prefill_summary(pw, pw.calls[0], min(args.steps, 10),
-                                                     max(args.warmup, 3))
-            del pw
-            torch.cuda.empty_cache()
-
-    # the rows beyond the core path run after the headline legs
-    if (not args.no_next and call.kind == "decode" and len(wl.calls) == 1
-            and wl.name == "decode_64"):
+    if "next" in legs:
         log("rows beyond the core path: grouped heads, append, page copy, windows")
-        result["next_rows"] = next_rows_summary(wl, args.steps, args.warmup)
+        dwl = workloads.get("decode_64") or W.decode_64(device="cuda")
+        result["next_rows"] = next_rows_summary(dwl, args.steps, args.warmup)
+
+    if not args.no_digest:
+        log("SHA-256 of every input buffer")
+        result["input_sha256"] = {name: wl.digest() for name, wl in workloads.items()}
+        if "config" in result and result["config"].get("workload") in result["input_sha256"]:
+            result["config"]["input_sha256"] = result["input_sha256"][result["config"]["workload"]]
 
     # the oracle runs last, after every GPU leg, so its host time cannot idle the GPU
     # between a warm-up and a timed region
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) on a bounded sample")
-        if call.kind == "decode":
-            result["cpu_baseline"] = cpu_baseline_decode(wl, call)
-        else:
-            result["cpu_baseline"] = cpu_baseline_prefill(wl, call)
-    del wl
+        todo = {k: v for k, v in kept.items() if k in BASELINE_LEGS}
+        if todo:
+            import shutil
+            import tempfile
+            log(f"cpu baseline (oracle) on {cpu_workers()} processes: {sorted(todo)}")
+            scratch = tempfile.mkdtemp(prefix="pa_oracle_",
+                                       dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+            try:
+                samples = {k: (wl, call, out, baseline_samples(k, wl, call))
+                           for k, (wl, call, out) in todo.items()}
+                result["cpu_baseline"] = cpu_baseline(samples, scratch)
+            finally:
+                shutil.rmtree(scratch, ignore_errors=True)
 
     print(json.dumps(result), flush=True)
 

@@ -88,10 +88,15 @@ class Workload:
         return self.q_heads or self.heads
 
     def digest(self) -> str:
-        """SHA-256 over every input buffer (host copies), for the record."""
+        """SHA-256 over every input buffer (host copies, streamed in 128 MiB pieces),
+        for the record: K pool, V pool, then each call's queries, block table, lengths
+        and chunk offsets."""
         h = hashlib.sha256()
         for t in [self.k_pool, self.v_pool] + [c.q for c in self.calls]:
-            h.update(t.detach().view(torch.int16).cpu().numpy().tobytes())
+            flat = t.detach().contiguous().view(-1).view(torch.int16)
+            step = 1 << 26
+            for s in range(0, flat.numel(), step):
+                h.update(flat[s:s + step].cpu().numpy().tobytes())
         for c in self.calls:
             h.update(c.block_table_host.tobytes())
             h.update(c.seq_lens_host.tobytes())

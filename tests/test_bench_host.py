@@ -1,4 +1,6 @@
 """Host-side arithmetic of bench.py: algorithmic work counts against brute force."""
+import os
+
 import numpy as np
 
 import bench
@@ -121,3 +123,41 @@ def test_more_than_one_gpu_is_refused():
         bench.os.path.abspath(bench.__file__)), capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_pool_on_small_workloads(tmp_path, monkeypatch):
+    """The bench's oracle pool on two small workloads: per-leg rates, the process count,
+    the CPU model, and parity figures against stand-in outputs (the oracle's own values
+    rounded to bf16, well inside the tolerance)."""
+    import torch
+    from exact_tiled_attention_pa_amd import workloads as W
+    from tests.oracle_pins import to_bf16_bits
+
+    monkeypatch.setattr(bench, "cpu_workers", lambda: 2)
+    dec = W.build("decode_64", 5, heads=2, head_dim=64, page_size=16, lens=[40, 300, 17],
+                  kind="decode", pool_slack=1.3, device="cpu", q_heads=4)
+    pre = W.build("prefill_32k", 6, heads=2, head_dim=64, page_size=16, lens=[200],
+                  q_lens=[200], causal=True, device="cpu")
+    legs = {}
+    for name, wl in (("decode_64", dec), ("prefill_32k", pre)):
+        call = wl.calls[0]
+        q = W.to_host_bits(call.q)
+        k, v = W.to_host_bits(wl.k_pool), W.to_host_bits(wl.v_pool)
+        if call.kind == "decode":
+            ref, _ = OA.paged_decode(q, k, v, call.block_table_host, call.seq_lens_host, wl.scale)
+        else:
+            ref, _ = OA.paged_prefill(q, k, v, call.block_table_host, call.seq_lens_host,
+                                      call.q_start_host, True, wl.scale)
+        out = torch.from_numpy(to_bf16_bits(ref).view(np.int16)).view(torch.bfloat16)
+        legs[name] = (wl, call, out, bench.baseline_samples(name, wl, call))
+    res = bench.cpu_baseline(legs, str(tmp_path))
+    assert res["cores"] == 2 and res["kind"] == "oracle" and res["cpu_model"]
+    assert res["unit"] == "GB/s" and res["value"] > 0
+    d, p = res["legs"]["decode_64"], res["legs"]["prefill_32k"]
+    assert d["unit"] == "GB/s" and p["unit"] == "TFLOP/s" and p["value"] > 0
+    for leg in (d, p):
+        assert leg["parity"]["within_tolerance"], leg
+        assert leg["parity"]["max_abs"] <= 1e-2
+    # the prefill sample: every 8th row from row 4, all heads
+    assert p["parity"]["elements"] == len(range(4, 200, 8)) * 2 * 64
+    assert os.listdir(tmp_path) == []

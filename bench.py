@@ -208,13 +208,19 @@ def timed_decode(wl, call, out, steps, warmup):
     return wall, [e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev]
 
 
-def timed_launches(fn, steps, warmup):
+def timed_launches(fn, steps, warmup, warm_s=0.0):
     """(wall s, HIP-event durations in ms) of `steps` launches of fn on torch's current
-    stream, after `warmup` untimed ones."""
+    stream, after `warmup` untimed ones and, with warm_s > 0, after untimed launches
+    for at least warm_s seconds (the chip's clock settles under sustained load)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
@@ -255,6 +261,13 @@ def decode_leg(wl, call, steps, warmup):
     return res, out
 
 
+# untimed prefill launches before each prefill leg's timed region: the shader clock
+# takes tens of milliseconds of sustained MFMA load to settle after the chip has idled
+# (input generation between legs); half a second reaches the steady state a serving
+# loop runs at
+PREFILL_WARM_S = 0.5
+
+
 def prefill_leg(wl, call, steps, warmup):
     """prefill: FLOPs of the visible pairs against 2.5 PFLOP/s, per launch."""
     import torch
@@ -266,7 +279,7 @@ def prefill_leg(wl, call, steps, warmup):
         B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
                      call.causal, wl.scale, out, call.q_start, call.max_q_len)
 
-    wall, ms = timed_launches(run, steps, warmup)
+    wall, ms = timed_launches(run, steps, warmup, warm_s=PREFILL_WARM_S)
     roof = _rate(flops, ms, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
                  kernel=f"prefill_kernel<{wl.head_dim}, {str(call.causal).lower()}>")
     wl_key = wl.name if len(wl.calls) == 1 else f"{wl.name}_chunks"

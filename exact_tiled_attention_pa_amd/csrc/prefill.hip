@@ -31,7 +31,11 @@
 //     transposing V reads (ds_read_b64_tr_b16) are free of bank conflicts;
 //   - two LDS stages: tile j+1 streams in while tile j is computed; one barrier
 //     per tile.  The loads of tile j+1 are issued after tile j's S^T MFMAs, so the
-//     scalar work of the issue runs while those MFMAs execute.
+//     scalar work of the issue runs while those MFMAs execute;
+//   - the block-table entries of tile j+1 are fetched during tile j-1 and waited for
+//     right after tile j's barrier, when no LDS read is outstanding: scalar loads and
+//     LDS reads share one completion counter, so a table wait placed after the tile's
+//     LDS reads would also hold the softmax until the V^T reads had returned.
 //
 // Per key tile (per wave, 32 query rows):
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q stays in VGPRs for the whole
@@ -177,6 +181,23 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     }
   }
 
+  // Physical pages of this wave's loads of one tile, fetched one tile ahead of their
+  // use so that the scalar loads' wait never lands among outstanding LDS reads.
+  int tbl[G::kInstPerWave];
+#pragma unroll
+  for (int i = 0; i < G::kInstPerWave; ++i) tbl[i] = 0;
+  auto fetch_table = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < G::kInstPerWave; ++i) {
+      const int first_row = G::kRowsPerInst * (kWaves * i + wave);
+      const int t0 = j * BN + (first_row & ~15);
+      tbl[i] = bt[min(t0 >> log2_ps, last_page)];
+    }
+  };
+  auto table_ready = [&]() {
+#pragma unroll
+    for (int i = 0; i < G::kInstPerWave; ++i) __asm__ __volatile__("" ::"s"(tbl[i]));
+  };
   // Streams tile j (64 keys from position 64j) of K and V into one LDS stage.
   auto issue_tile = [&](int j, char* k_dst, char* v_dst) {
     const int kt0 = j * BN;
@@ -184,7 +205,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     for (int i = 0; i < G::kInstPerWave; ++i) {
       const int first_row = G::kRowsPerInst * (kWaves * i + wave);
       const int t0 = kt0 + (first_row & ~15);       // first token of the 16-row group
-      const int phys = bt[min(t0 >> log2_ps, last_page)];
+      const int phys = tbl[i];
       const int valid = min(16, seq_len - t0);      // rows of the group below seq_len
       const int bytes = valid > 0 ? valid * row_bytes_g : 0;
       const size_t elem =
@@ -327,15 +348,21 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
   auto step = [&](int j, char* k_cur, char* v_cur, char* k_nxt, char* v_nxt) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j landed
     __syncthreads();                     // everyone's loads landed; tile j-1 fully consumed
+    table_ready();                       // tile j+1's pages (no LDS read outstanding here)
     // a tile wholly in this wave's causal future, or wholly before its window, is skipped
     const bool skip = CAUSAL && (j * BN > wave_last_pos || j * BN + BN - 1 < wave_lo);
     if (!skip) scores(j, k_cur, v_cur);
     if (j + 1 < n_tiles) issue_tile(j + 1, k_nxt, v_nxt);
+    if (j + 2 < n_tiles) fetch_table(j + 2);
     if (skip) return;
     finish_tile(j);
   };
 
-  if (first_tile < n_tiles) issue_tile(first_tile, k_lds0, v_lds0);
+  if (first_tile < n_tiles) {
+    fetch_table(first_tile);
+    issue_tile(first_tile, k_lds0, v_lds0);
+    if (first_tile + 1 < n_tiles) fetch_table(first_tile + 1);
+  }
   for (int j = first_tile; j < n_tiles; j += 2) {
     step(j, k_lds0, v_lds0, k_lds1, v_lds1);
     if (j + 1 < n_tiles) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);

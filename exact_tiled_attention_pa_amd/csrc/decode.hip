@@ -7,10 +7,10 @@
 // the cache reads dominate).  The design therefore aims only at moving bytes the
 // way HBM likes them:
 //
-//   pass 1 (decode_partial_kernel): grid (head group, split, sequence).  A head
-//     group is the heads one wave load covers: 64 lanes x 16 B = 1 KB = one
-//     token's row for 4 consecutive heads at d = 128 (8 at d = 64), contiguous in
-//     the pool's [page, slot, head, d] layout.  Consecutive workgroups are the
+//   pass 1 (decode_partial_kernel): grid (head group, split, sequence), the two inner
+//     coordinates rotated by the sequence index.  A head group is the heads one wave
+//     load covers: 64 lanes x 16 B = 1 KB = one token's row for 4 consecutive heads at
+//     d = 128 (8 at d = 64), contiguous in the pool's [page, slot, head, d] layout.  Consecutive workgroups are the
 //     head groups of the same key range, so concurrently running workgroups read
 //     adjacent kilobytes of the same token rows (DRAM row locality), instead of
 //     256-byte pieces 8 KB apart.  A split is a range of split_tokens key
@@ -72,10 +72,12 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   constexpr uint32_t kAllBytes = 0x7fffffffu;  // buffer size: offsets are checked here
   __shared__ __attribute__((aligned(1024))) char ring[kRingBytes];
 
-  const int hg = blockIdx.x;
   const int b = blockIdx.z;
+  // grid rows and columns rotated by the sequence index: see rotated_grid_index
+  const int hg = rotated_grid_index(blockIdx.x, gridDim.x, b);
   const int seq_len = seq_lens[b];
-  const int split = decode_split_of(blockIdx.y, seq_len, split_tokens, window);
+  const int split =
+      decode_split_of(rotated_grid_index(blockIdx.y, gridDim.y, b), seq_len, split_tokens, window);
   if (split < 0) return;
   const int t_begin = split * split_tokens;
   if (t_begin >= seq_len) return;  // the combine pass never reads this split

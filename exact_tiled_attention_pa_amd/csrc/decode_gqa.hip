@@ -8,8 +8,9 @@
 // kernel therefore treats the g query heads of one token like the rows of a small
 // query tile and runs both contractions on the matrix cores:
 //
-//   grid  (K/V head x head block, split, sequence).  A head block is up to 32 of the
-//         g query heads (one MFMA operand's worth); g > 32 takes several blocks.
+//   grid  (K/V head x head block, split, sequence), both inner coordinates rotated by
+//         the sequence index.  A head block is up to 32 of the g query heads (one MFMA
+//         operand's worth); g > 32 takes several blocks.
 //         Splits are the same key ranges as the one-head-per-row decode, and the
 //         partials go to the same workspace, so the same combine pass finishes.
 //   block 4 waves.  The split's keys come in tiles of 32 positions; wave w takes
@@ -76,13 +77,17 @@ decode_gqa_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
   const int group = num_q_heads / num_kv_heads;
   const int blocks_per_kv = (group + kHeadBlock - 1) / kHeadBlock;
-  const int hk = blockIdx.x / blocks_per_kv;
-  const int hb = blockIdx.x % blocks_per_kv;
+  const int b = blockIdx.z;
+  // grid rows and columns rotated by the sequence index (a bijection per sequence): see
+  // rotated_grid_index
+  const int col = rotated_grid_index(blockIdx.x, gridDim.x, b);
+  const int hk = col / blocks_per_kv;
+  const int hb = col % blocks_per_kv;
   const int h0 = hk * group + hb * kHeadBlock;          // first query head of the block
   const int nh = min(kHeadBlock, group - hb * kHeadBlock);
-  const int b = blockIdx.z;
   const int seq_len = seq_lens[b];
-  const int split = decode_split_of(blockIdx.y, seq_len, split_tokens, window);
+  const int split =
+      decode_split_of(rotated_grid_index(blockIdx.y, gridDim.y, b), seq_len, split_tokens, window);
   if (split < 0) return;
   const int t_begin = split * split_tokens;
   if (t_begin >= seq_len) return;  // the combine pass never reads this split

@@ -73,6 +73,17 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Decode grids are (columns, rows, sequence) with many rows past a short sequence's
+// last split.  The hardware deals a kernel's workgroups to the shader engines of an XCD
+// in launch order, round robin, and dispatches them in order, so an engine that keeps
+// receiving the costly low rows paces its whole XCD while the others idle.  Rotating
+// each sequence's rows (and columns) by its index spreads every sequence's live splits
+// evenly over the engines; it is a bijection per sequence, so each split is still
+// computed by exactly one workgroup.
+__device__ __forceinline__ int rotated_grid_index(int i, int n, int seq) {
+  return (int)(((unsigned)i + (unsigned)seq) % (unsigned)n);
+}
+
 // Split walked by decode grid row y (see decode_grid_splits): with a sliding window the
 // rows count back from the sequence's last split, else row y is split y.  Negative:
 // nothing to do.

@@ -692,6 +692,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-digest", action="store_true",
                     help="skip the SHA-256 of every input buffer")
+    ap.add_argument("--prefill-warm-s", type=float, default=0.5,
+                    help="seconds of untimed launches before each prefill leg (profiling "
+                         "runs shorten it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
@@ -704,6 +707,7 @@ def main():
     ap.add_argument("--profile-command", default="",
                     help="the command recorded in a summary")
     args = ap.parse_args()
+    globals()["PREFILL_WARM_S"] = args.prefill_warm_s
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.profile_command)
         return
@@ -782,10 +786,14 @@ def main():
                    "prefill_32k": "prefill_long", "prefill_600": "prefill_600"}[leg]
             result[key] = res
         log(f"leg {leg}: done")
-    if "value" not in result:  # no decode leg: the first leg's rate heads the line
-        first = next(k for k in ("prefill", "prefill_noncausal", "prefill_long", "prefill_600")
-                     if k in result)
-        s = result[first]
+    if "value" not in result and "mixed" in result:  # the mixed batch's decode heads it
+        d = result["mixed"]["decode"]
+        result.update({"value": d["gbs"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
+                       "config": {"workload": d["workload"]}, "roofline": d["roofline"]})
+    prefills = [k for k in ("prefill", "prefill_noncausal", "prefill_long", "prefill_600")
+                if k in result]
+    if "value" not in result and prefills:  # no decode leg: the first prefill leg heads it
+        s = result[prefills[0]]
         result.update({"value": s["tflops"], "unit": "TFLOP/s",
                        "ms_per_step": round(s["us_per_call_wall"] / 1e3, 4),
                        "config": {"workload": s["workload"], "causal": s["causal"]},
@@ -795,6 +803,11 @@ def main():
         log("rows beyond the core path: grouped heads, append, page copy, windows")
         dwl = workloads.get("decode_64") or W.decode_64(device="cuda")
         result["next_rows"] = next_rows_summary(dwl, args.steps, args.warmup)
+        if "value" not in result:  # only these rows ran: the grouped-head decode heads it
+            g = result["next_rows"]["gqa_decode"]
+            result.update({"value": g["achieved"], "unit": g["unit"],
+                           "ms_per_step": g["kernel_ms_avg"],
+                           "config": {"workload": g["workload"]}, "roofline": g})
 
     if not args.no_digest:
         log("SHA-256 of every input buffer")

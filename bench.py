@@ -178,40 +178,89 @@ def _ms(st, key):
     return round(st[key], 4)
 
 
+def region_ms(fn, steps):
+    """(wall s, ms per call) of `steps` back-to-back calls of fn, timed by one pair of
+    HIP events around them on torch's current stream (the stream the library launches
+    on) and by the host clock."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+
+
+def paired_ms(fn, steps):
+    """HIP-event duration (ms) of each of `steps` calls of fn, one event pair per call."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+class Timing:
+    """A kernel's timed launches: `avg` (ms) from one event pair around `steps`
+    back-to-back launches, the kernel's average launch duration; `pairs`, each launch of a
+    second run of `steps` timed by its own event pair, for the median and minimum (the
+    event commands between launches add 1-2 us to each of these)."""
+
+    def __init__(self, avg, pairs):
+        self.avg = avg
+        self.pairs = pairs
+
+
 def timed_decode(wl, call, out, steps, warmup):
-    """K decode steps (pass 1 + combine, each bracketed by HIP events on torch's current
-    stream, the stream the library launches on); returns (wall s, pass-1 ms, combine ms)."""
+    """K decode steps (pass 1 + combine); returns (wall s per K whole steps, pass-1
+    Timing, combine Timing)."""
     import torch
     from exact_tiled_attention_pa_amd import binding as B
     ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
     lay = B.layout_of(wl.k_pool, call.block_table)
 
-    def step():
+    def partial():
         B.pa_decode_partial(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
                             wl.scale, ws)
+
+    def combine():
         B.pa_decode_combine(call.seq_lens, out, ws, lay)
+
+    def step():
+        partial()
+        combine()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    wall, _ = region_ms(step, steps)
+    _, p_avg = region_ms(partial, steps)
+    _, c_avg = region_ms(combine, steps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        B.pa_decode_partial(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
-                            wl.scale, ws)
+        partial()
         ev[i][1].record()
-        B.pa_decode_combine(call.seq_lens, out, ws, lay)
+        combine()
         ev[i][2].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, [e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev]
+    step()  # the output of one whole step, for the digests and the baseline
+    torch.cuda.synchronize()
+    return (wall, Timing(p_avg, [e[0].elapsed_time(e[1]) for e in ev]),
+            Timing(c_avg, [e[1].elapsed_time(e[2]) for e in ev]))
 
 
 def timed_launches(fn, steps, warmup, warm_s=0.0):
-    """(wall s, HIP-event durations in ms) of `steps` launches of fn on torch's current
-    stream, after `warmup` untimed ones and, with warm_s > 0, after untimed launches
-    for at least warm_s seconds (the chip's clock settles under sustained load)."""
+    """(wall s, Timing) of `steps` launches of fn on torch's current stream, after
+    `warmup` untimed ones and, with warm_s > 0, after untimed launches for at least
+    warm_s seconds (the chip's clock settles under sustained load)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -221,26 +270,20 @@ def timed_launches(fn, steps, warmup, warm_s=0.0):
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record()
-        fn()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, [e[0].elapsed_time(e[1]) for e in ev]
+    wall, avg = region_ms(fn, steps)
+    return wall, Timing(avg, paired_ms(fn, steps))
 
 
-def _rate(work, ms, peak, unit, **extra):
-    """Rate of one kernel against its peak from the average event-timed launch, with the
-    median and minimum beside it."""
-    st = timing_stats(ms)
+def _rate(work, timing, peak, unit, **extra):
+    """Rate of one kernel against its peak from its average launch duration, with the
+    median and minimum of the per-launch timings beside it."""
+    st = timing_stats(timing.pairs)
     scale = 1e9 if unit == "GB/s" else 1e12
-    achieved = work / (st["avg"] * 1e-3) / scale
+    achieved = work / (timing.avg * 1e-3) / scale
     return dict(extra, achieved=round(achieved, 2), unit=unit, peak=peak,
-                frac=round(achieved / peak, 4), kernel_ms_avg=_ms(st, "avg"),
-                kernel_ms_median=_ms(st, "median"), kernel_ms_min=_ms(st, "min"))
+                frac=round(achieved / peak, 4), kernel_ms_avg=round(timing.avg, 4),
+                kernel_ms_median=_ms(st, "median"), kernel_ms_min=_ms(st, "min"),
+                kernel_ms_avg_paired=_ms(st, "avg"))
 
 
 def decode_leg(wl, call, steps, warmup):
@@ -248,13 +291,13 @@ def decode_leg(wl, call, steps, warmup):
     import torch
     nbytes = decode_kv_bytes(wl, call)
     out = torch.empty_like(call.q)
-    wall, split_ms, comb_ms = timed_decode(wl, call, out, steps, warmup)
+    wall, split_t, comb_t = timed_decode(wl, call, out, steps, warmup)
     ms_step = wall / steps * 1e3
-    roof = _rate(nbytes, split_ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+    roof = _rate(nbytes, split_t, HBM_PEAK_GBS, "GB/s", bound="hbm",
                  kernel=decode_kernel_name(wl))
-    cst = timing_stats(comb_ms)
+    cst = timing_stats(comb_t.pairs)
     roof.update(traffic=recorded_traffic(decode_kind(wl), wl.name),
-                combine_ms_avg=_ms(cst, "avg"), combine_ms_median=_ms(cst, "median"))
+                combine_ms_avg=round(comb_t.avg, 4), combine_ms_median=_ms(cst, "median"))
     res = {"workload": wl.name, "gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
            "ms_per_step": round(ms_step, 4), "kv_bytes_per_step": nbytes,
            "total_tokens": int(call.seq_lens_host.sum()), "roofline": roof}
@@ -279,8 +322,8 @@ def prefill_leg(wl, call, steps, warmup):
         B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
                      call.causal, wl.scale, out, call.q_start, call.max_q_len)
 
-    wall, ms = timed_launches(run, steps, warmup, warm_s=PREFILL_WARM_S)
-    roof = _rate(flops, ms, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
+    wall, tm = timed_launches(run, steps, warmup, warm_s=PREFILL_WARM_S)
+    roof = _rate(flops, tm, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
                  kernel=f"prefill_kernel<{wl.head_dim}, {str(call.causal).lower()}>")
     wl_key = wl.name if len(wl.calls) == 1 else f"{wl.name}_chunks"
     roof.update(traffic=recorded_traffic("prefill", wl_key),
@@ -322,13 +365,13 @@ def next_rows_summary(decode_wl, steps, warmup):
     ws = B.decode_workspace(call.q, decode_wl.k_pool, call.block_table)
     out = torch.empty_like(call.q)
     w = 1024
-    _, ms = timed_launches(lambda: B.pa_decode(call.q, decode_wl.k_pool, decode_wl.v_pool,
+    _, tm = timed_launches(lambda: B.pa_decode(call.q, decode_wl.k_pool, decode_wl.v_pool,
                                                call.block_table, call.seq_lens,
                                                decode_wl.scale, out, ws, window=w),
                            steps, warmup)
     seen = np.minimum(call.seq_lens_host.astype(np.int64), w).sum()
     nbytes = int(seen) * 2 * decode_wl.heads * decode_wl.head_dim * 2
-    res["window_decode"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+    res["window_decode"] = _rate(nbytes, tm, HBM_PEAK_GBS, "GB/s", bound="hbm",
                                  workload=f"decode_64, window {w}",
                                  kernel="decode_partial_kernel<128> + decode_combine_kernel<128>")
     del ws, out
@@ -337,10 +380,10 @@ def next_rows_summary(decode_wl, steps, warmup):
     g = W.decode_64_gqa8(device="cuda")
     gc = g.calls[0]
     ws = B.decode_workspace(gc.q, g.k_pool, gc.block_table)
-    _, ms = timed_launches(lambda: B.pa_decode_partial(gc.q, g.k_pool, g.v_pool,
+    _, tm = timed_launches(lambda: B.pa_decode_partial(gc.q, g.k_pool, g.v_pool,
                                                        gc.block_table, gc.seq_lens, g.scale,
                                                        ws), steps, warmup)
-    res["gqa_decode"] = _rate(decode_kv_bytes(g, gc), ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+    res["gqa_decode"] = _rate(decode_kv_bytes(g, gc), tm, HBM_PEAK_GBS, "GB/s", bound="hbm",
                               workload=g.name, kernel=decode_kernel_name(g),
                               traffic=recorded_traffic("decode_gqa", g.name))
     del g, gc, ws
@@ -354,10 +397,10 @@ def next_rows_summary(decode_wl, steps, warmup):
     v_new = W.normal_bf16((n_tok, heads, d), 1.0, 13, "cuda")
     ids = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
     pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
-    _, ms = timed_launches(lambda: B.pa_kv_append(k_new, v_new, ids, pos, a.k_pool, a.v_pool,
+    _, tm = timed_launches(lambda: B.pa_kv_append(k_new, v_new, ids, pos, a.k_pool, a.v_pool,
                                                   ac.block_table), steps, warmup)
     nbytes = n_tok * heads * d * 2 * 2 * 2  # K and V rows, read once and written once
-    res["kv_append"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+    res["kv_append"] = _rate(nbytes, tm, HBM_PEAK_GBS, "GB/s", bound="hbm",
                              workload="append_4096: 4096 tokens, 32 K/V heads, d=128, "
                                       "pages of 16, shuffled", kernel="kv_append_kernel")
     del a, ac, k_new, v_new, ids, pos
@@ -369,10 +412,10 @@ def next_rows_summary(decode_wl, steps, warmup):
     perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(16))
     src = perm[:n_pairs].to(torch.int32).cuda()
     dst = perm[n_pairs:2 * n_pairs].to(torch.int32).cuda()
-    _, ms = timed_launches(lambda: B.pa_copy_pages(kp, vp, src, dst), steps, warmup)
+    _, tm = timed_launches(lambda: B.pa_copy_pages(kp, vp, src, dst), steps, warmup)
     page_bytes = ps * heads * d * 2
     nbytes = n_pairs * page_bytes * 2 * 2  # both pools, read and write
-    res["copy_pages"] = _rate(nbytes, ms, HBM_PEAK_GBS, "GB/s", bound="hbm",
+    res["copy_pages"] = _rate(nbytes, tm, HBM_PEAK_GBS, "GB/s", bound="hbm",
                               workload=f"copy_2048: {n_pairs} page pairs of 16 tokens x 32 "
                                        "heads x d=128", kernel="copy_pages_kernel")
     del kp, vp, src, dst
@@ -382,13 +425,14 @@ def next_rows_summary(decode_wl, steps, warmup):
     pc = p.calls[0]
     out = torch.empty_like(pc.q)
     w = 4096
-    _, ms = timed_launches(lambda: B.pa_prefill(pc.q, p.k_pool, p.v_pool, pc.block_table,
+    _, tm = timed_launches(lambda: B.pa_prefill(pc.q, p.k_pool, p.v_pool, pc.block_table,
                                                 pc.seq_lens, True, p.scale, out, pc.q_start,
-                                                pc.max_q_len, window=w), steps, warmup)
+                                                pc.max_q_len, window=w), steps, warmup,
+                           warm_s=PREFILL_WARM_S)
     n = int(pc.seq_lens_host[0])
     pairs = w * (w + 1) // 2 + (n - w) * w
     flops = 4 * p.head_dim * pc.q.shape[1] * pairs
-    res["window_prefill"] = _rate(flops, ms, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
+    res["window_prefill"] = _rate(flops, tm, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
                                   workload=f"prefill_32k, window {w}",
                                   kernel="prefill_kernel<128, true>")
     del p, pc, out

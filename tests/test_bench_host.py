@@ -161,3 +161,16 @@ def test_cpu_baseline_pool_on_small_workloads(tmp_path, monkeypatch):
     # the prefill sample: every 8th row from row 4, all heads
     assert p["parity"]["elements"] == len(range(4, 200, 8)) * 2 * 64
     assert os.listdir(tmp_path) == []
+
+
+def test_rate_takes_the_average_from_the_whole_timed_region():
+    """`achieved` and `frac` come from the average over one event pair around all timed
+    launches; median, minimum and the per-launch-pair average come from the second run."""
+    import bench
+
+    t = bench.Timing(2.0, [2.5, 2.1, 2.2, 3.0])
+    r = bench._rate(8e12, t, 2500.0, "TFLOP/s", bound="mfma")
+    assert r["kernel_ms_avg"] == 2.0 and r["achieved"] == 4000.0
+    assert r["frac"] == round(4000.0 / 2500.0, 4)
+    assert r["kernel_ms_median"] == 2.35 and r["kernel_ms_min"] == 2.1
+    assert r["kernel_ms_avg_paired"] == 2.45 and r["bound"] == "mfma"

@@ -147,6 +147,8 @@ def _poison(pool: torch.Tensor, tables, lens_list, page_size):
     for table, lens in zip(tables, lens_list):
         for b, L in enumerate(lens):
             n = _pages_of(L, page_size)
+            if n == 0:  # an empty sequence reads nothing
+                continue
             pages = table[b, :n]
             used[pages[:-1], :] = True
             used[pages[-1], :int(L) - (n - 1) * page_size] = True

@@ -365,6 +365,25 @@ def test_empty_batch_and_zero_rows_are_no_ops():
     assert st == B.PA_OK and torch.all(out == 3.0)
 
 
+@pytest.mark.parametrize("hq,window", [(2, 0), (2, 100), (16, 0), (16, 100)])
+def test_decode_empty_sequences_get_zeros(hq, window):
+    """A sequence with L_b = 0 reads nothing (its table row holds only -1) and its output
+    rows are exactly zero; the other sequences of the batch match the oracle.  hq=16 over
+    2 K/V heads runs the grouped kernel, hq=2 the one-head-per-row kernel."""
+    G.banner(f"decode with empty sequences Hq={hq} window={window}")
+    wl = W.build("z", 3, heads=2, head_dim=128, page_size=16, lens=[0, 37, 0, 1300, 0],
+                 kind="decode", pool_slack=1.2, device="cuda", poison=True, q_heads=hq)
+    call = wl.calls[0]
+    out = torch.full_like(call.q, 7.0)
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale, out,
+                ws, window=window)
+    torch.cuda.synchronize()
+    got = G.bf16_out_to_f64(out)
+    assert np.all(got[[0, 2, 4]] == 0.0)
+    G.compare(got, G.oracle_for(wl, call, seqs=[1, 3], window=window), "decode, empty seqs")
+
+
 # ----------------------------------------------------------------- sliding window
 
 WINDOW_PREFILL_CASES = [

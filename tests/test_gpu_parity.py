@@ -550,3 +550,38 @@ def test_decode_agrees_with_last_prefill_row(hq):
     torch.cuda.synchronize()
     G.compare(G.bf16_out_to_f64(out), G.bf16_out_to_f64(pre.index_select(0, last)),
               "decode vs prefill last row", max_tol=8e-3, mean_tol=5e-4)
+
+
+def test_prefill_131072_tokens_sampled():
+    """One 131,072-token causal sequence (1 head, d=128, shuffled pages of 256): 1024
+    query tiles, up to 2048 key tiles per workgroup; rows spread over the sequence."""
+    G.banner("prefill N=131072, 1 head, rows sampled")
+    n = 131072
+    wl = W.build("pf_128k", 23, heads=1, head_dim=128, page_size=256, lens=[n], q_lens=[n],
+                 causal=True, device="cuda")
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(24)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 65535, 65536, n - 129, n - 128, n - 1],
+                                     rng.integers(0, n, 12)]))
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, rows={0: rows}),
+              "prefill N=131072")
+
+
+@pytest.mark.parametrize("hq", [1, 4])
+def test_decode_batch_at_the_api_limit(hq):
+    """65,535 sequences (the most one call accepts, the largest grid dimension) of 1-40
+    cached tokens, 1 K/V head, d=64: 400 sampled sequences, the first and the last
+    included, against the oracle."""
+    G.banner(f"decode batch 65535 Hq={hq}")
+    rng = np.random.default_rng(25)
+    lens = [int(x) for x in rng.integers(1, 41, size=65535)]
+    wl = W.build("dec_65535", 26, heads=1, head_dim=64, page_size=16, lens=lens,
+                 kind="decode", pool_slack=1.1, device="cuda", q_heads=hq)
+    call = wl.calls[0]
+    out = G.run_call(wl, call)
+    torch.cuda.synchronize()
+    seqs = sorted(set([0, 65534] + [int(x) for x in rng.integers(0, 65535, 398)]))
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, seqs=seqs),
+              f"decode batch 65535 Hq={hq}")

@@ -162,6 +162,13 @@ def decode_kind(wl) -> str:
     return "decode_gqa" if wl.num_q_heads // wl.heads >= GQA_MIN_GROUP else "decode"
 
 
+def prefill_kernel_name(wl, causal) -> str:
+    """The prefill instantiation a workload runs: head dim, causal, and whether a key tile
+    of 64 lies in one page (pages of 64 tokens or more)."""
+    return (f"prefill_kernel<{wl.head_dim}, {str(bool(causal)).lower()}, "
+            f"{str(wl.page_size >= 64).lower()}>")
+
+
 def decode_kernel_name(wl) -> str:
     return f"{KERNEL_FILES[decode_kind(wl)]}<{wl.head_dim}>"
 
@@ -324,7 +331,7 @@ def prefill_leg(wl, call, steps, warmup):
 
     wall, tm = timed_launches(run, steps, warmup, warm_s=PREFILL_WARM_S)
     roof = _rate(flops, tm, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
-                 kernel=f"prefill_kernel<{wl.head_dim}, {str(call.causal).lower()}>")
+                 kernel=prefill_kernel_name(wl, call.causal))
     wl_key = wl.name if len(wl.calls) == 1 else f"{wl.name}_chunks"
     roof.update(traffic=recorded_traffic("prefill", wl_key),
                 mfma_busy=recorded_mfma("prefill", wl_key))
@@ -434,7 +441,7 @@ def next_rows_summary(decode_wl, steps, warmup):
     flops = 4 * p.head_dim * pc.q.shape[1] * pairs
     res["window_prefill"] = _rate(flops, tm, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
                                   workload=f"prefill_32k, window {w}",
-                                  kernel="prefill_kernel<128, true>")
+                                  kernel=prefill_kernel_name(p, True))
     del p, pc, out
     torch.cuda.empty_cache()
     return res
@@ -618,8 +625,8 @@ def baseline_samples(name, wl, call):
 # ------------------------------------------------------------------ rocprofv3 summaries
 
 KERNEL_TAGS = {"decode": "decode_partial_kernel", "decode_gqa": "decode_gqa_kernel",
-               "prefill": "prefill_kernel<128, true>",
-               "prefill_noncausal": "prefill_kernel<128, false>"}
+               "prefill": "prefill_kernel<128, true",
+               "prefill_noncausal": "prefill_kernel<128, false"}
 
 
 def _read_csv(path):

@@ -20,7 +20,10 @@
 // K/V tile staging (no VGPR round trip, no per-element address arithmetic):
 //   - a 64-key tile is 4 groups of 16 keys; a group never straddles a page (pages
 //     hold a power of two >= 16 tokens), so its physical page is one scalar
-//     block-table load and its address one scalar base;
+//     block-table load and its address one scalar base; with pages of 64 tokens or
+//     more the whole tile lies in one page, so each wave reads one table entry per
+//     tile and derives its groups' bases from that page's address by a scalar add
+//     (a separate instantiation: half the scalar work of the tile issue);
 //   - each wave issues buffer loads straight into LDS (16 B per lane, 1 KB per
 //     instruction) against a buffer resource whose base is the group's first row
 //     and whose size covers only the rows below the sequence length: rows past
@@ -85,7 +88,8 @@ struct Geometry {
   static constexpr int kStageOut = D + 8;                  // epilogue row stride (elements)
 };
 
-template <int D, bool CAUSAL>
+// LARGE_PAGES: page_size >= BN, so a key tile never straddles a page.
+template <int D, bool CAUSAL, bool LARGE_PAGES>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
                const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
@@ -181,26 +185,51 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
     }
   }
 
-  // Physical pages of this wave's loads of one tile, fetched one tile ahead of their
-  // use so that the scalar loads' wait never lands among outstanding LDS reads.
-  int tbl[G::kInstPerWave];
+  // Physical pages of this wave's loads of one tile (with large pages, the tile's one
+  // page), fetched one tile ahead of their use so that the scalar loads' wait never
+  // lands among outstanding LDS reads.
+  constexpr int kTablePerTile = LARGE_PAGES ? 1 : G::kInstPerWave;
+  int tbl[kTablePerTile];
 #pragma unroll
-  for (int i = 0; i < G::kInstPerWave; ++i) tbl[i] = 0;
+  for (int i = 0; i < kTablePerTile; ++i) tbl[i] = 0;
   auto fetch_table = [&](int j) {
 #pragma unroll
-    for (int i = 0; i < G::kInstPerWave; ++i) {
+    for (int i = 0; i < kTablePerTile; ++i) {
       const int first_row = G::kRowsPerInst * (kWaves * i + wave);
-      const int t0 = j * BN + (first_row & ~15);
+      const int t0 = j * BN + (LARGE_PAGES ? 0 : (first_row & ~15));
       tbl[i] = bt[min(t0 >> log2_ps, last_page)];
     }
   };
   auto table_ready = [&]() {
 #pragma unroll
-    for (int i = 0; i < G::kInstPerWave; ++i) __asm__ __volatile__("" ::"s"(tbl[i]));
+    for (int i = 0; i < kTablePerTile; ++i) __asm__ __volatile__("" ::"s"(tbl[i]));
   };
   // Streams tile j (64 keys from position 64j) of K and V into one LDS stage.
   auto issue_tile = [&](int j, char* k_dst, char* v_dst) {
     const int kt0 = j * BN;
+    if constexpr (LARGE_PAGES) {
+      // the tile's 64 rows are consecutive rows of one page: one 64-bit page address,
+      // then each 16-row group's base and size (its rows below seq_len) by scalar adds
+      const int valid = min(BN, seq_len - kt0);
+      const size_t elem =
+          (((size_t)tbl[0] << log2_ps) + (kt0 & ps_mask)) * (size_t)num_kv_heads * D;
+      const char* const kb = reinterpret_cast<const char*>(k_pool + elem);
+      const char* const vb = reinterpret_cast<const char*>(v_pool + elem);
+#pragma unroll
+      for (int i = 0; i < G::kInstPerWave; ++i) {
+        const int first_row = G::kRowsPerInst * (kWaves * i + wave);
+        const int g = first_row & ~15;  // first row of the group inside the tile
+        const int rows = min(16, valid - g);
+        const int bytes = rows > 0 ? rows * row_bytes_g : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(kb + g * row_bytes_g, bytes),
+                                                 (lds_void*)(k_dst + first_row * G::kRowBytes),
+                                                 16, k_voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(vb + g * row_bytes_g, bytes),
+                                                 (lds_void*)(v_dst + first_row * G::kRowBytes),
+                                                 16, v_voff, 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < G::kInstPerWave; ++i) {
       const int first_row = G::kRowsPerInst * (kWaves * i + wave);
@@ -400,14 +429,20 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
   }
 }
 
-template <int D, bool CAUSAL>
-void launch(const PrefillArgs& a, hipStream_t stream) {
+template <int D, bool CAUSAL, bool LARGE_PAGES>
+void launch_pages(const PrefillArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.max_q_len + BM - 1) / BM;
   const dim3 grid(a.num_q_heads, n_qtiles, a.batch);
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a.q,
-                     a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.q_start, a.out,
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, LARGE_PAGES>), grid, dim3(kThreads), 0, stream,
+                     a.q, a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.q_start, a.out,
                      score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
                      a.log2_page_size, a.max_pages_per_seq, a.window);
+}
+
+template <int D, bool CAUSAL>
+void launch(const PrefillArgs& a, hipStream_t stream) {
+  if ((1 << a.log2_page_size) >= BN) launch_pages<D, CAUSAL, true>(a, stream);
+  else launch_pages<D, CAUSAL, false>(a, stream);
 }
 
 }  // namespace

@@ -34,8 +34,8 @@ def test_mfma_busy_fraction_from_a_counter_run(tmp_path):
     # shader cycles per launch = SQ_CYCLES / 32 engines; busy cycles summed over 1024 SIMDs
     for disp, (busy, sq) in {"7": (0.5 * 1024 * 300000, 32 * 300000),
                              "9": (0.25 * 1024 * 200000, 32 * 200000)}.items():
-        rows.append([disp, "pa::prefill_kernel<128, true>", "SQ_VALU_MFMA_BUSY_CYCLES", busy])
-        rows.append([disp, "pa::prefill_kernel<128, true>", "SQ_CYCLES", sq])
+        rows.append([disp, "pa::prefill_kernel<128, true, true>", "SQ_VALU_MFMA_BUSY_CYCLES", busy])
+        rows.append([disp, "pa::prefill_kernel<128, true, true>", "SQ_CYCLES", sq])
     rows.append(["8", "pa::decode_partial_kernel<128>", "SQ_VALU_MFMA_BUSY_CYCLES", 1.0])
     rows.append(["8", "pa::decode_partial_kernel<128>", "SQ_CYCLES", 1.0])
     with open(tmp_path / "run_counter_collection.csv", "w", newline="") as f:
@@ -98,7 +98,7 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
             w.writerow(["1", "__amd_rocclr_copyBuffer", "1048576", counter, copy_kib])
             w.writerow(["2", "__amd_rocclr_copyBuffer", "64", counter, 1.0])  # small copy
             for i, v in enumerate(kernel_kib):
-                w.writerow([str(3 + i), "pa::prefill_kernel<128, true>", "262144", counter, v])
+                w.writerow([str(3 + i), "pa::prefill_kernel<128, true, true>", "262144", counter, v])
             w.writerow(["9", "pa::decode_partial_kernel<128>", "262144", counter, 1e9])
         return str(d)
 

@@ -14,14 +14,17 @@
 //     head groups of the same key range, so concurrently running workgroups read
 //     adjacent kilobytes of the same token rows (DRAM row locality), instead of
 //     256-byte pieces 8 KB apart.  A split is a range of split_tokens key
-//     positions (whole pages).  Its keys are streamed in steps of 16 tokens, each
-//     of the 4 waves taking 4 consecutive tokens of a step, with buffer loads that
-//     write straight into a per-wave ring of LDS slots (no VGPR staging, so the
-//     kernel needs few registers and the ring, not the register file, sets how
-//     many bytes are in flight: 4 steps = 32 KB per wave, 128 KB per CU).  Each
-//     lane reads its own 16 bytes back from LDS.  The physical page of every
-//     16-token chunk comes from the block table ("What is Paged FlashAttention?",
-//     "Practical example"), fetched for the whole split by one vector load.
+//     positions (whole pages); with a sliding window the splits start at the
+//     window's first key (rounded down to a multiple of 4), so a window of w keys
+//     takes ceil(w / split_tokens) workgroups per head group and none walks keys
+//     before it.  Its keys are streamed in steps of 16 tokens, each of the 4 waves
+//     taking 4 consecutive tokens of a step, with buffer loads that write straight
+//     into a per-wave ring of LDS slots (no VGPR staging, so the kernel needs few
+//     registers and the ring, not the register file, sets how many bytes are in
+//     flight: 4 steps = 32 KB per wave, 128 KB per CU).  Each lane reads its own 16
+//     bytes back from LDS.  The physical page of every page the split touches comes
+//     from the block table ("What is Paged FlashAttention?", "Practical example"),
+//     one page per lane, fetched for the whole split by one vector load.
 //     Dot products run on the VALU and are summed over the 16 lanes of a head
 //     with DPP moves; every 16-lane row group keeps its own online-softmax state
 //     (running max m, running sum l, output accumulator; "Flash Attention: Fast,
@@ -76,16 +79,23 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // grid rows and columns rotated by the sequence index: see rotated_grid_index
   const int hg = rotated_grid_index(blockIdx.x, gridDim.x, b);
   const int seq_len = seq_lens[b];
-  const int split =
-      decode_split_of(rotated_grid_index(blockIdx.y, gridDim.y, b), seq_len, split_tokens, window);
-  if (split < 0) return;
-  const int t_begin = split * split_tokens;
-  if (t_begin >= seq_len) return;  // the combine pass never reads this split
-  const int t_end = min(seq_len, t_begin + split_tokens);
-  // sliding window: only the last `window` keys count; earlier splits are skipped by
-  // both passes
+  const int split = rotated_grid_index(blockIdx.y, gridDim.y, b);
+  // sliding window: only the last `window` keys count (t_lo on)
   const int t_lo = window > 0 ? max(0, seq_len - window) : 0;
-  if (t_end <= t_lo) return;
+  int t_begin, t_end;
+  if (window > 0) {
+    // splits laid from t_lo rounded down to a multiple of 4 (a wave's 4 consecutive
+    // tokens then never straddle a page); the last one runs to the sequence end and
+    // holds up to 3 keys more than split_tokens
+    const int n_splits = window_split_count(seq_len, window, split_tokens);
+    if (split >= n_splits) return;  // the combine pass never reads this split
+    t_begin = (t_lo & ~3) + split * split_tokens;
+    t_end = split == n_splits - 1 ? seq_len : t_begin + split_tokens;
+  } else {
+    t_begin = split * split_tokens;
+    if (t_begin >= seq_len) return;  // the combine pass never reads this split
+    t_end = min(seq_len, t_begin + split_tokens);
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -112,11 +122,13 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
   }
 
-  // physical page of each chunk of the split, one per lane (split_tokens <= 64 * 16)
+  // physical page of each page the split touches, one per lane (a split holds at most
+  // split_tokens + 3 <= 259 keys, so at most 18 pages of 16)
   const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
-  int chunk_page = 0;
-  if (lane < n_chunks)
-    chunk_page = block_table[(size_t)b * max_pages + ((t_begin + lane * kChunk) >> log2_ps)];
+  const int page0 = t_begin >> log2_ps;
+  int split_page = 0;
+  if (lane <= ((t_end - 1) >> log2_ps) - page0)
+    split_page = block_table[(size_t)b * max_pages + page0 + lane];
   // these loads complete here: the ring's loads below are not tracked by the compiler,
   // so no wait it would place for these may be left to count them
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -130,7 +142,8 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int t0 = t_begin + s * kChunk + wave * kStep;
     const uint32_t slot = ring_base + (uint32_t)((s % kRing) * kSlotBytes);
     const bool live = s < n_chunks;
-    const int phys = live ? __builtin_amdgcn_readlane(chunk_page, min(s, 63)) : 0;
+    const int phys =
+        live ? __builtin_amdgcn_readlane(split_page, min((t0 >> log2_ps) - page0, 63)) : 0;
     const size_t row0 = (((size_t)phys << log2_ps) + (t0 & ps_mask)) * (size_t)token_bytes;
     const u32x4 rk = buffer_words(reinterpret_cast<const char*>(k_pool) + row0, kAllBytes);
     const u32x4 rv = buffer_words(reinterpret_cast<const char*>(v_pool) + row0, kAllBytes);
@@ -254,15 +267,21 @@ template <int D>
 __global__ void __launch_bounds__(kCombineThreads)
 decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restrict__ ws_o,
                       const float* __restrict__ ws_ml, uint16_t* __restrict__ out,
-                      int num_q_heads, int split_tokens, int max_splits, int window) {
+                      int num_q_heads, int split_tokens, int max_splits, int window,
+                      int window_aligned) {
   constexpr int kPerLane = D / 64;
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.x * kCombineHeads + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (h >= num_q_heads) return;
   const int b = blockIdx.y;
   const int seq_len = seq_lens[b];
-  const int n_splits = seq_len > 0 ? (seq_len + split_tokens - 1) / split_tokens : 0;
-  const int s_first = window > 0 ? max(0, seq_len - window) / split_tokens : 0;
+  // splits holding keys: with a window, the window-aligned splits of the
+  // one-head-per-row decode (0 .. count - 1), or the grouped-head decode's splits from
+  // the one holding the window's first key
+  int s_first = 0;
+  int n_splits = seq_len > 0 ? (seq_len + split_tokens - 1) / split_tokens : 0;
+  if (window > 0 && window_aligned) n_splits = window_split_count(seq_len, window, split_tokens);
+  else if (window > 0) s_first = max(0, seq_len - window) / split_tokens;
   const size_t slot0 = ((size_t)b * num_q_heads + h) * max_splits;
 
   float m = kEmptyMax, l = 0.f;
@@ -313,7 +332,7 @@ void launch_partial(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_q_heads / a.num_kv_heads >= kGqaMinGroup) return launch_decode_partial_gqa(a, stream);
+  if (decode_grouped(a)) return launch_decode_partial_gqa(a, stream);
   if (a.head_dim == 128) launch_partial<128>(a, stream);
   else launch_partial<64>(a, stream);
   return hipGetLastError();
@@ -324,11 +343,11 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(kCombineThreads), 0, stream,
                        a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
-                       a.max_splits, a.window);
+                       a.max_splits, a.window, decode_grouped(a) ? 0 : 1);
   } else {
     hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(kCombineThreads), 0, stream,
                        a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
-                       a.max_splits, a.window);
+                       a.max_splits, a.window, decode_grouped(a) ? 0 : 1);
   }
   return hipGetLastError();
 }

@@ -84,9 +84,9 @@ __device__ __forceinline__ int rotated_grid_index(int i, int n, int seq) {
   return (int)(((unsigned)i + (unsigned)seq) % (unsigned)n);
 }
 
-// Split walked by decode grid row y (see decode_grid_splits): with a sliding window the
-// rows count back from the sequence's last split, else row y is split y.  Negative:
-// nothing to do.
+// Split walked by grouped-head decode grid row y (see decode_grid_splits): with a
+// sliding window the rows count back from the sequence's last split, else row y is
+// split y.  Negative: nothing to do.
 __device__ __forceinline__ int decode_split_of(int y, int seq_len, int split_tokens,
                                                int window) {
   return window > 0 ? (seq_len > 0 ? (seq_len - 1) / split_tokens : 0) - y : y;

@@ -49,13 +49,30 @@ struct DecodeArgs {
   int window;  // sliding-window length (0: none)
 };
 
-// Decode grids: with a sliding window only the splits that can hold keys inside it
-// are launched, counted back from each sequence's last split (a window of w keys
-// touches at most ceil(w / split_tokens) + 1 splits); grid row y then walks split
-// (L_b - 1) / split_tokens - y (decode_split_of).  Without a window row y is split y.
+// Query heads per K/V head from which decode reads each K/V page once per group.
+constexpr int kGqaMinGroup = 4;
+
+inline bool decode_grouped(const DecodeArgs& a) {
+  return a.num_q_heads / a.num_kv_heads >= kGqaMinGroup;
+}
+
+// Splits of a windowed one-head-per-row decode: they start at the window's first key
+// rounded down to a multiple of 4 and the last one runs to the sequence end, so a
+// window of w keys takes ceil(min(w, L) / split_tokens) splits (decode.hip).
+__host__ __device__ inline int window_split_count(int seq_len, int window, int split_tokens) {
+  const int w = seq_len < window ? seq_len : window;
+  return w > 0 ? (w + split_tokens - 1) / split_tokens : 0;
+}
+
+// Decode grids.  Without a window row y is split y.  With a sliding window only the
+// splits that can hold keys inside it are launched: the one-head-per-row decode walks
+// the window-aligned splits above; the grouped-head decode keeps the splits at
+// multiples of split_tokens and counts back from each sequence's last split (a window
+// of w keys touches at most ceil(w / split_tokens) + 1 of them), grid row y walking
+// split (L_b - 1) / split_tokens - y (decode_split_of).
 inline int decode_grid_splits(const DecodeArgs& a) {
   if (a.window <= 0) return a.max_splits;
-  const int n = (a.window + a.split_tokens - 1) / a.split_tokens + 1;
+  const int n = (a.window + a.split_tokens - 1) / a.split_tokens + (decode_grouped(a) ? 1 : 0);
   return n < a.max_splits ? n : a.max_splits;
 }
 
@@ -94,9 +111,6 @@ constexpr int kPrefillBlockN = 64;
 constexpr int kDecodeSplitTokens = 256;
 // Keys per decode split with grouped heads (at most 64 groups of 16 keys).
 constexpr int kDecodeSplitTokensGrouped = 1024;
-
-// Query heads per K/V head from which decode reads each K/V page once per group.
-constexpr int kGqaMinGroup = 4;
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);

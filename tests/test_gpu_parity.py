@@ -428,6 +428,27 @@ def test_decode_sliding_window(window, hq):
     G.compare(G.bf16_out_to_f64(out), ref, f"decode window={window} Hq={hq}")
 
 
+@pytest.mark.parametrize("window,ps", [(1024, 16), (259, 16), (257, 64), (1024, 256),
+                                       (513, 256), (3, 32)])
+def test_decode_window_split_alignment(window, ps):
+    """The one-head-per-row decode lays a window's splits from its first key rounded down
+    to a multiple of 4, the last split running to the sequence end: lengths put that
+    first key at every residue mod 4 and on both sides of page and split boundaries."""
+    G.banner(f"decode window split alignment window={window} ps={ps}")
+    lens = [window + r for r in (0, 1, 2, 3, 5, 17, 255, 256, 257)] + [1, window - 1, 4099]
+    lens = [max(1, x) for x in lens]
+    wl = W.build("walign", 500 + window + ps, heads=4, head_dim=128, page_size=ps, lens=lens,
+                 kind="decode", pool_slack=1.2, device="cuda", poison=True)
+    call = wl.calls[0]
+    out = torch.empty_like(call.q)
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale, out,
+                ws, window=window)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, window=window),
+              f"decode window={window} ps={ps}")
+
+
 def test_window_one_returns_own_value_row():
     """w = 1: every query sees only its own key, so O is exactly its own V row."""
     G.banner("window=1 exactness")

@@ -108,6 +108,18 @@ size_t ws_ml_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layou
   return (n * sizeof(float) + 255) / 256 * 256;
 }
 
+// Pass 1's plan of the one-head-per-row decode: a claim counter, the number of
+// (sequence, split) pairs and the pairs themselves.
+size_t ws_plan_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
+  const size_t n = 2 + (size_t)batch * max_splits_of(layout, num_q_heads);
+  return (n * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+size_t ws_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
+  return ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout) +
+         ws_plan_bytes(batch, num_q_heads, layout);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
@@ -131,8 +143,12 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
   if (max_splits_of(layout, num_q_heads) > 65535)
     return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size = %lld needs more than 65535 "
                 "decode splits", (long long)layout->max_pages_per_seq * layout->page_size);
+  // pass 1 numbers its units of work (split x head group) with 32-bit integers
+  if ((int64_t)batch * max_splits_of(layout, num_q_heads) * num_q_heads >= ((int64_t)1 << 31))
+    return fail(PA_ERR_INVALID_ARG, "%d sequences x %d splits x %d query heads exceed 2^31 "
+                "decode work units", batch, max_splits_of(layout, num_q_heads), num_q_heads);
   if (!check_workspace) return PA_OK;
-  const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
+  const size_t need = ws_bytes(batch, num_q_heads, layout);
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (!aligned16(workspace))
     return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -157,6 +173,8 @@ pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf1
   char* ws = static_cast<char*>(const_cast<void*>(workspace));
   a.ws_o = reinterpret_cast<float*>(ws);
   a.ws_ml = reinterpret_cast<float*>(ws + ws_o_bytes(batch, num_q_heads, layout));
+  a.plan = reinterpret_cast<int32_t*>(ws + ws_o_bytes(batch, num_q_heads, layout) +
+                                      ws_ml_bytes(batch, num_q_heads, layout));
   a.scale = scale;
   a.batch = batch;
   a.num_q_heads = num_q_heads;
@@ -242,7 +260,7 @@ int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                  const pa_kv_layout* layout) {
   if (check_layout(layout, num_q_heads) != PA_OK || batch < 0) return 0;
-  return ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
+  return ws_bytes(batch, num_q_heads, layout);
 }
 
 int32_t pa_decode_split_tokens(int32_t num_q_heads, const pa_kv_layout* layout) {
@@ -311,7 +329,7 @@ int pa_decode_noalloc(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_
                                num_q_heads, nullptr, 0, layout, true, false);
   if (st) return st;
   if (!out) return fail(PA_ERR_NULL, "out must be non-NULL");
-  const size_t need = ws_o_bytes(batch, num_q_heads, layout) + ws_ml_bytes(batch, num_q_heads, layout);
+  const size_t need = ws_bytes(batch, num_q_heads, layout);
   if (need > PA_NOALLOC_SCRATCH_BYTES)
     return fail(PA_ERR_WORKSPACE,
                 "pa_decode_noalloc: %d sequences x %d query heads over up to %lld tokens need "

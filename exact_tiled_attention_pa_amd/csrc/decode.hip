@@ -7,30 +7,30 @@
 // the cache reads dominate).  The design therefore aims only at moving bytes the
 // way HBM likes them:
 //
-//   pass 1 (decode_partial_kernel): grid (head group, split, sequence), the two inner
-//     coordinates rotated by the sequence index.  A head group is the heads one wave
-//     load covers: 64 lanes x 16 B = 1 KB = one token's row for 4 consecutive heads at
-//     d = 128 (8 at d = 64), contiguous in the pool's [page, slot, head, d] layout.  Consecutive workgroups are the
-//     head groups of the same key range, so concurrently running workgroups read
-//     adjacent kilobytes of the same token rows (DRAM row locality), instead of
-//     256-byte pieces 8 KB apart.  A split is a range of split_tokens key
-//     positions (whole pages); with a sliding window the splits start at the
-//     window's first key (rounded down to a multiple of 4), so a window of w keys
-//     takes ceil(w / split_tokens) workgroups per head group and none walks keys
-//     before it.  Its keys are streamed in steps of 16 tokens, each of the 4 waves
-//     taking 4 consecutive tokens of a step, with buffer loads that write straight
-//     into a per-wave ring of LDS slots (no VGPR staging, so the kernel needs few
-//     registers and the ring, not the register file, sets how many bytes are in
-//     flight: 4 steps = 32 KB per wave, 128 KB per CU).  Each lane reads its own 16
-//     bytes back from LDS.  The physical page of every page the split touches comes
-//     from the block table ("What is Paged FlashAttention?", "Practical example"),
-//     one page per lane, fetched for the whole split by one vector load.
-//     Dot products run on the VALU and are summed over the 16 lanes of a head
-//     with DPP moves; every 16-lane row group keeps its own online-softmax state
-//     (running max m, running sum l, output accumulator; "Flash Attention: Fast,
-//     Memory-Efficient Attention for LLMs", "The Algorithm"), the 4 waves' states
-//     are merged through LDS and the split's (m, l, unnormalised O) goes to the
-//     workspace.
+//   pass 1 (decode_plan_kernel, then decode_partial_kernel): the work is a list of
+//     (sequence, split) pairs, a split being 256 consecutive keys (with a sliding
+//     window the splits are laid back from the sequence end, so a window of w keys
+//     takes ceil(w / 256) of them), times the head groups: a head group is the heads
+//     one wave load covers, 64 lanes x 16 B = 1 KB = one token's row for 4 adjacent
+//     heads at d = 128 (8 at d = 64), contiguous in the pool's [page, slot, head, d]
+//     layout.  A one-workgroup plan pass lists the pairs and zeroes a claim counter in
+//     the workspace.  Pass 1 then runs one persistent workgroup per CU: eight waves
+//     stream K/V, one more (the scheduler) claims units from the counter, resolves
+//     each (its sequence, its table pages "What is Paged FlashAttention?", "Practical
+//     example", its query slice) into an LDS descriptor a unit ahead, and merges and
+//     stores each finished unit's partial.  The streaming waves take 4 consecutive
+//     tokens each of every 32-token step with 16-byte non-temporal buffer loads into
+//     registers, one step in flight while the previous one is consumed, and run on
+//     from one unit into the next without draining: the scheduler issues every other
+//     vector memory operation, so their wait counts cover only their own loads.  A
+//     workgroup that streams for the whole launch moves far more bytes per second than
+//     a short one per unit, which pays its first loads' latency each time (measured on
+//     plain streaming probes: 6.2 TB/s with a 512 KB workgroup each, 7.0 persistent).
+//     Dot products run on the VALU and are summed over the 16 lanes of a head with DPP
+//     moves; every 16-lane row group keeps its own online-softmax state (running max
+//     m, running sum l, output accumulator; "Flash Attention: Fast, Memory-Efficient
+//     Attention for LLMs", "The Algorithm"); the waves' states are merged through LDS
+//     and the unit's (m, l, unnormalised O) goes to the workspace.
 //   pass 2 (decode_combine_kernel): one wave per (sequence, head) merges the
 //     splits' partials in order with the same rescaling algebra and writes bf16 O.
 //
@@ -44,13 +44,21 @@
 namespace pa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = 16;                   // tokens per chunk (never straddles a page)
-constexpr int kStep = kChunk / kWaves;       // consecutive tokens of a chunk per wave
-constexpr int kRing = 5;                     // LDS slots per wave: 4 steps in flight
-constexpr int kSlotBytes = kStep * 2 * 1024; // the step's K rows, then its V rows
+constexpr int kStreamWaves = 8;                       // waves that stream K/V
+constexpr int kThreads = (kStreamWaves + 1) * 64;     // plus one scheduler wave
+constexpr int kStep = 4;                     // consecutive tokens of a step per wave
+constexpr int kChunk = kStep * kStreamWaves; // tokens per step of a split
+constexpr int kRing = 2;                     // register slots per streaming wave
+constexpr int kAhead = kRing - 1;            // steps in flight ahead of the one consumed
+constexpr int kQueue = 4;                    // split descriptors held in LDS
+constexpr int kItemPages = 32;               // pages one split may touch (<= 17 here)
+constexpr int kSplitTokensMha = 256;         // keys per split (kDecodeSplitTokens)
+constexpr int kSplitSteps = kSplitTokensMha / kChunk;  // 8 steps of 32 keys
+constexpr int kMidStep = 4;                  // step at which the next split is published
+static_assert(kSplitSteps % kRing == 0, "every split starts in ring slot 0");
+static_assert(kSplitSteps - kAhead >= kMidStep, "the next split is known before its loads");
 constexpr float kEmptyMax = -1e30f;          // running max before any visible key (finite)
+constexpr int kPlanThreads = 1024;
 
 template <int D>
 struct DecodeGeometry {
@@ -58,101 +66,259 @@ struct DecodeGeometry {
   static constexpr int kHeads = 64 / kLanesPerHead;    // heads per wave load
 };
 
+// One claimed unit of work: a split of one sequence for one head group, resolved by
+// the scheduler wave (page numbers and the query slice included) for the streaming
+// waves.
+struct SplitDesc {
+  int valid, b, split, hg;
+  int t_begin, t_end, t_lo, page0;
+  int pages[kItemPages];  // physical pages page0, page0 + 1, ... of the split
+  u32x4 q[64];            // the head group's query rows, lane l's 16 bytes at q[l]
+  uint32_t loff[64];      // lane l's byte offset inside a token row (absent head: past it)
+};
+
+template <int D>
+struct DecodeShared {
+  SplitDesc desc[kQueue];
+  // each streaming wave's (O, m, l) per head at the end of a split, double-buffered
+  float mo[2][kStreamWaves][DecodeGeometry<D>::kHeads][D];
+  float mm[2][kStreamWaves][DecodeGeometry<D>::kHeads];
+  float ml[2][kStreamWaves][DecodeGeometry<D>::kHeads];
+};
+
+// Workgroup barrier that waits only for this wave's LDS traffic: the streaming waves'
+// buffer-to-LDS loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Split key range [t_begin, t_end) of split `split` of a sequence of seq_len keys.
+// Without a window split s covers keys 256 s .. 256 s + 255; with a sliding window the
+// splits are laid back from the sequence end, so a window of w keys takes
+// ceil(min(w, L) / 256) splits of at most 256 keys, the first one reaching back to the
+// window's first key (keys before it are masked).
+__device__ __forceinline__ void split_range(int seq_len, int split, int window, int& t_begin,
+                                            int& t_end) {
+  if (window > 0) {
+    const int n = window_split_count(seq_len, window, kSplitTokensMha);
+    t_end = seq_len - (n - 1 - split) * kSplitTokensMha;
+    t_begin = max(0, t_end - kSplitTokensMha);
+  } else {
+    t_begin = split * kSplitTokensMha;
+    t_end = min(seq_len, t_begin + kSplitTokensMha);
+  }
+}
+
+// The list of (sequence, split) pairs holding keys, in sequence order, and the claim
+// counter of pass 1, both in the workspace: plan[0] = counter (zeroed here), plan[1] =
+// number of pairs, plan[2 + i] = pair i as the unsigned (sequence << 16) | split.  One workgroup
+// scans the sequences' split counts.
+__global__ void __launch_bounds__(kPlanThreads)
+decode_plan_kernel(const int32_t* __restrict__ seq_lens, int batch, int split_tokens,
+                   int max_splits, int window, int32_t* __restrict__ plan) {
+  __shared__ int scan[kPlanThreads];
+  int base = 0;
+  for (int c = 0; c < batch; c += kPlanThreads) {
+    const int b = c + (int)threadIdx.x;
+    int n = 0;
+    if (b < batch) {
+      const int len = seq_lens[b];
+      n = window > 0 ? window_split_count(len, window, split_tokens)
+                     : (len > 0 ? (len + split_tokens - 1) / split_tokens : 0);
+      n = min(n, max_splits);  // the plan and the partials hold max_splits per sequence
+    }
+    scan[threadIdx.x] = n;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const int add = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += add;
+      __syncthreads();
+    }
+    const int first = base + scan[threadIdx.x] - n;
+    // packed unsigned: sequence indices reach 65534, past the int32 sign bit once shifted
+    for (int i = 0; i < n; ++i) plan[2 + first + i] = (int32_t)(((uint32_t)b << 16) | (uint32_t)i);
+    base += scan[kPlanThreads - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    plan[0] = 0;
+    plan[1] = base;
+  }
+}
+
+// Pass 1: one persistent workgroup per CU.  The scheduler wave claims splits from the
+// plan's counter two ahead of the streaming waves, resolves each (sequence, table
+// pages, query slice) into an LDS descriptor, and merges and writes the partial of the
+// split the streaming waves finished last; it issues every vector memory operation
+// besides the K/V stream, so the streaming waves' wait counts cover their own loads
+// only and their stream runs on across split boundaries without draining.
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
                       const uint16_t* __restrict__ v_pool,
                       const int32_t* __restrict__ block_table,
                       const int32_t* __restrict__ seq_lens, float* __restrict__ ws_o,
-                      float* __restrict__ ws_ml, float scale_log2, int num_q_heads,
-                      int num_kv_heads, int log2_ps, int max_pages, int split_tokens,
-                      int max_splits, int window) {
+                      float* __restrict__ ws_ml, int32_t* __restrict__ plan,
+                      float scale_log2, int num_q_heads, int num_kv_heads, int log2_ps,
+                      int max_pages, int max_splits, int window) {
   using G = DecodeGeometry<D>;
-  constexpr int kRingBytes = kWaves * kRing * kSlotBytes;  // 160 KB: one workgroup per CU
-  constexpr int kMergeBytes = (kWaves * G::kHeads * D + 2 * kWaves * G::kHeads) * 4;
-  static_assert(kMergeBytes <= kRingBytes, "the merge arrays reuse the ring");
   constexpr uint32_t kOutside = 0x80000000u;   // a load offset past every buffer
   constexpr uint32_t kAllBytes = 0x7fffffffu;  // buffer size: offsets are checked here
-  __shared__ __attribute__((aligned(1024))) char ring[kRingBytes];
-
-  const int b = blockIdx.z;
-  // grid rows and columns rotated by the sequence index: see rotated_grid_index
-  const int hg = rotated_grid_index(blockIdx.x, gridDim.x, b);
-  const int seq_len = seq_lens[b];
-  const int split = rotated_grid_index(blockIdx.y, gridDim.y, b);
-  // sliding window: only the last `window` keys count (t_lo on)
-  const int t_lo = window > 0 ? max(0, seq_len - window) : 0;
-  int t_begin, t_end;
-  if (window > 0) {
-    // splits laid from t_lo rounded down to a multiple of 4 (a wave's 4 consecutive
-    // tokens then never straddle a page); the last one runs to the sequence end and
-    // holds up to 3 keys more than split_tokens
-    const int n_splits = window_split_count(seq_len, window, split_tokens);
-    if (split >= n_splits) return;  // the combine pass never reads this split
-    t_begin = (t_lo & ~3) + split * split_tokens;
-    t_end = split == n_splits - 1 ? seq_len : t_begin + split_tokens;
-  } else {
-    t_begin = split * split_tokens;
-    if (t_begin >= seq_len) return;  // the combine pass never reads this split
-    t_end = min(seq_len, t_begin + split_tokens);
-  }
+  __shared__ __attribute__((aligned(1024))) DecodeShared<D> sh;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_hg = (num_q_heads + G::kHeads - 1) / G::kHeads;
   const int row = lane / G::kLanesPerHead;
   const int col = lane % G::kLanesPerHead;
-  const int h = hg * G::kHeads + row;          // query head of this row group
-  const bool active = h < num_q_heads;
-  const int hk = (active ? h : 0) / (num_q_heads / num_kv_heads);
+
+  if (wave == kStreamWaves) {
+    // ------------------------------------------------------------- scheduler wave
+    const int n_items = plan[1] * n_hg;
+    struct Claim { int valid, b, split, hg; };
+    auto resolve = [&](SplitDesc& d) -> Claim {
+      int qi = 0;
+      if (lane == 0) qi = atomicAdd(&plan[0], 1);
+      qi = __builtin_amdgcn_readfirstlane(qi);
+      Claim c{0, 0, 0, 0};
+      if (qi >= n_items) {
+        if (lane == 0) d.valid = 0;
+        return c;
+      }
+      const uint32_t pair = (uint32_t)plan[2 + qi / n_hg];
+      c = Claim{1, (int)(pair >> 16), (int)(pair & 0xffffu), qi % n_hg};
+      const int seq_len = seq_lens[c.b];
+      int t_begin, t_end;
+      split_range(seq_len, c.split, window, t_begin, t_end);
+      const int page0 = t_begin >> log2_ps;
+      if (lane <= ((t_end - 1) >> log2_ps) - page0)
+        d.pages[lane] = block_table[(size_t)c.b * max_pages + page0 + lane];
+      const int h = c.hg * G::kHeads + row;
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if (h < num_q_heads)
+        w = *reinterpret_cast<const u32x4*>(q + ((size_t)c.b * num_q_heads + h) * D + col * 8);
+      d.q[lane] = w;
+      d.loff[lane] = h < num_q_heads
+                         ? (uint32_t)(((h / (num_q_heads / num_kv_heads)) * D + col * 8) * 2)
+                         : 0x80000000u;
+      if (lane == 0) {
+        d.valid = 1;
+        d.b = c.b;
+        d.split = c.split;
+        d.hg = c.hg;
+        d.t_begin = t_begin;
+        d.t_end = t_end;
+        d.t_lo = window > 0 ? max(0, seq_len - window) : 0;
+        d.page0 = page0;
+      }
+      return c;
+    };
+    // the streaming waves' states of a finished split -> its partial in the workspace
+    auto merge = [&](const Claim& c, int buf) {
+      for (int idx = lane; idx < G::kHeads * D; idx += 64) {
+        const int r = idx / D;
+        const int d = idx % D;
+        const int hh = c.hg * G::kHeads + r;
+        if (hh >= num_q_heads) continue;
+        float big = sh.mm[buf][0][r];
+#pragma unroll
+        for (int w = 1; w < kStreamWaves; ++w) big = fmaxf(big, sh.mm[buf][w][r]);
+        float acc = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kStreamWaves; ++w) {
+          const float wt = fast_exp2(sh.mm[buf][w][r] - big);
+          acc = fmaf(wt, sh.mo[buf][w][r][d], acc);
+          lsum = fmaf(wt, sh.ml[buf][w][r], lsum);
+        }
+        const size_t slot = ((size_t)c.b * num_q_heads + hh) * max_splits + c.split;
+        ws_o[slot * D + d] = acc;
+        if (d == 0) {
+          ws_ml[slot * 2] = big;
+          ws_ml[slot * 2 + 1] = lsum;
+        }
+      }
+    };
+    Claim prev{0, 0, 0, 0};
+    Claim cur = resolve(sh.desc[0]);
+    lds_barrier();  // split 0 published
+    for (int k = 0;; ++k) {
+      if (!cur.valid) {
+        if (prev.valid) merge(prev, (k - 1) & 1);
+        break;
+      }
+      const Claim nxt = resolve(sh.desc[(k + 1) % kQueue]);
+      lds_barrier();  // mid-split: split k + 1 published
+      if (prev.valid) merge(prev, (k - 1) & 1);
+      lds_barrier();  // end of split k: its states are in mo/mm/ml[k & 1]
+      prev = cur;
+      cur = nxt;
+    }
+    return;
+  }
+
+  // --------------------------------------------------------------- streaming waves
   const int ps_mask = (1 << log2_ps) - 1;
   const int token_bytes = num_kv_heads * D * 2;  // bytes between tokens in the pools
-  // this lane's 16 bytes inside a token row; rows of absent heads load nothing
-  const uint32_t lane_off = active ? (uint32_t)((hk * D + col * 8) * 2) : kOutside;
 
-  // query slice of this lane, pre-multiplied by scale * log2(e)
+  // split being consumed (c_*) and split being issued ahead (n_*, once published)
+  int c_valid, c_tb, c_te, c_tlo, c_page0, c_pages, c_hg;
+  int n_valid = 0, n_tb = 0, n_te = 0, n_tlo = 0, n_page0 = 0, n_pages = 0;
   float qf[8];
-  {
-    u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (active)
-      w = *reinterpret_cast<const u32x4*>(q + ((size_t)b * num_q_heads + h) * D + col * 8);
+  uint32_t lane_off = kOutside, n_lane_off = kOutside;
+  auto load_desc = [&](const SplitDesc& d, int& valid, int& tb, int& te, int& tlo, int& page0,
+                       int& pages, int& hg) {
+    valid = __builtin_amdgcn_readfirstlane(d.valid);
+    tb = __builtin_amdgcn_readfirstlane(d.t_begin);
+    te = __builtin_amdgcn_readfirstlane(d.t_end);
+    tlo = __builtin_amdgcn_readfirstlane(d.t_lo);
+    page0 = __builtin_amdgcn_readfirstlane(d.page0);
+    hg = __builtin_amdgcn_readfirstlane(d.hg);
+    pages = d.pages[lane & (kItemPages - 1)];
+  };
+  auto load_query = [&](const SplitDesc& d) {
+    const u32x4 w = d.q[lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qf[2 * i] = bf16_lo(w[i]) * scale_log2;
       qf[2 * i + 1] = bf16_hi(w[i]) * scale_log2;
     }
-  }
+  };
 
-  // physical page of each page the split touches, one per lane (a split holds at most
-  // split_tokens + 3 <= 259 keys, so at most 18 pages of 16)
-  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
-  const int page0 = t_begin >> log2_ps;
-  int split_page = 0;
-  if (lane <= ((t_end - 1) >> log2_ps) - page0)
-    split_page = block_table[(size_t)b * max_pages + page0 + lane];
-  // these loads complete here: the ring's loads below are not tracked by the compiler,
-  // so no wait it would place for these may be left to count them
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // K/V rows of the steps in flight, in registers: step si of a split sits in slot
+  // si % kRing (a split is kSplitSteps steps, a multiple of kRing, so each starts in
+  // slot 0), token i of
+  // the wave's 4 at [slot][i]
+  u32x4 kr[kRing][kStep], vr[kRing][kStep];
 
-  // Step s = chunk s: this wave's tokens t_begin + 16 s + 4 w .. + 3 go to ring slot
-  // s % kRing.  Steps past the end are issued too, with every lane out of range (they
-  // write zeros to a free slot and read nothing), so each step is 8 loads and the
-  // waits below are constants.
-  const uint32_t ring_base = lds_address(ring) + (uint32_t)(wave * kRing * kSlotBytes);
-  auto issue = [&](int s) {
-    const int t0 = t_begin + s * kChunk + wave * kStep;
-    const uint32_t slot = ring_base + (uint32_t)((s % kRing) * kSlotBytes);
-    const bool live = s < n_chunks;
-    const int phys =
-        live ? __builtin_amdgcn_readlane(split_page, min((t0 >> log2_ps) - page0, 63)) : 0;
-    const size_t row0 = (((size_t)phys << log2_ps) + (t0 & ps_mask)) * (size_t)token_bytes;
-    const u32x4 rk = buffer_words(reinterpret_cast<const char*>(k_pool) + row0, kAllBytes);
-    const u32x4 rv = buffer_words(reinterpret_cast<const char*>(v_pool) + row0, kAllBytes);
+  // Step si of a split: its tokens t_begin + 32 si + 4 wave + i (i < 4), one 16-byte
+  // buffer load per token and pool.  Each token finds its own page (with windowed
+  // splits laid back from the sequence end a wave's 4 tokens may straddle two), and
+  // tokens outside the split's keys or before the window load with an offset past the
+  // buffer: zeros come back and nothing is read.  Branch-free, so that no register of a
+  // load still in flight is taken for a temporary on some path.
+  auto issue = [&](int valid, int tb, int te, int tlo, int page0, int pages, uint32_t loff,
+                   int si, u32x4* kd, u32x4* vd) {
+    const int t0 = tb + si * kChunk + wave * kStep;
+    const int te_eff = valid ? te : INT_MIN;  // an invalid split loads nothing
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
-      const bool ok = live && t0 + i < t_end && t0 + i >= t_lo;
-      const int voff = (int)(ok ? lane_off + (uint32_t)(i * token_bytes) : kOutside);
-      lds_load16(rk, slot + i * 1024, voff);
-      lds_load16(rv, slot + (kStep + i) * 1024, voff);
+      const int t = t0 + i;
+      const bool ok = t < te_eff && t >= tlo;
+      const int pidx = min(max((t >> log2_ps) - page0, 0), kItemPages - 1);
+      const int phys = __builtin_amdgcn_readlane(pages, pidx);
+      const size_t row = (((size_t)(uint32_t)phys << log2_ps) + (t & ps_mask)) * (size_t)token_bytes;
+      const __amdgpu_buffer_rsrc_t rk =
+          make_rsrc(reinterpret_cast<const char*>(k_pool) + row, (int)kAllBytes);
+      const __amdgpu_buffer_rsrc_t rv =
+          make_rsrc(reinterpret_cast<const char*>(v_pool) + row, (int)kAllBytes);
+      const int voff = (int)(ok ? loff : kOutside);
+      // non-temporal: every K/V byte is read once
+      kd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 2));
+      vd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 2));
     }
   };
 
@@ -161,15 +327,8 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
 
-  auto consume = [&](int s) {
-    const int t0 = t_begin + s * kChunk + wave * kStep;
-    const char* src = ring + wave * kRing * kSlotBytes + (s % kRing) * kSlotBytes + lane * 16;
-    u32x4 kc[kStep], vc[kStep];
-#pragma unroll
-    for (int i = 0; i < kStep; ++i) {
-      kc[i] = *reinterpret_cast<const u32x4*>(src + i * 1024);
-      vc[i] = *reinterpret_cast<const u32x4*>(src + (kStep + i) * 1024);
-    }
+  auto consume = [&](int si, const u32x4* kc, const u32x4* vc) {
+    const int t0 = c_tb + si * kChunk + wave * kStep;
     float sc[kStep];
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
@@ -180,7 +339,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         acc = fmaf(qf[2 * w + 1], bf16_hi(kc[i][w]), acc);
       }
       acc = group_sum<G::kLanesPerHead>(acc);
-      sc[i] = (t0 + i < t_end && t0 + i >= t_lo) ? acc : -INFINITY;
+      sc[i] = (t0 + i < c_te && t0 + i >= c_tlo) ? acc : -INFINITY;
     }
     float mx = sc[0];
 #pragma unroll
@@ -210,51 +369,64 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     m = m_new;
   };
 
+  lds_barrier();  // split 0 published
+  load_desc(sh.desc[0], c_valid, c_tb, c_te, c_tlo, c_page0, c_pages, c_hg);
+  if (!c_valid) return;
+  load_query(sh.desc[0]);
+  lane_off = sh.desc[0].loff[lane];
 #pragma unroll
-  for (int s = 0; s < kRing - 1; ++s) issue(s);
-  for (int s = 0; s < n_chunks; ++s) {
-    // slot (s - 1) % kRing was read back by the previous consume, whose arithmetic
-    // waited for those LDS reads, so it can take step s + kRing - 1 now
-    issue(s + kRing - 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kRing - 1) * 2 * kStep));  // step s landed
-    consume(s);
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();  // every wave is done with the ring, which now holds the merge arrays
+  for (int a = 0; a < kAhead; ++a)
+    issue(c_valid, c_tb, c_te, c_tlo, c_page0, c_pages, lane_off, a, kr[a], vr[a]);
 
-  // merge the 4 waves' states per head and write the split's partial
-  auto sm_o = reinterpret_cast<float (*)[G::kHeads][D]>(ring);
-  auto sm_m = reinterpret_cast<float (*)[G::kHeads]>(ring + kWaves * G::kHeads * D * 4);
-  auto sm_l = reinterpret_cast<float (*)[G::kHeads]>(ring + kWaves * G::kHeads * (D + 1) * 4);
+  for (int k = 0;; ++k) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) sm_o[wave][row][col * 8 + i] = o[i];
-  if (col == 0) {
-    sm_m[wave][row] = m;
-    sm_l[wave][row] = l;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G::kHeads * D; idx += kThreads) {
-    const int r = idx / D;
-    const int d = idx % D;
-    const int hh = hg * G::kHeads + r;
-    if (hh >= num_q_heads) continue;
-    float big = sm_m[0][r];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) big = fmaxf(big, sm_m[w][r]);
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(sm_m[w][r] - big);
-      acc = fmaf(wt, sm_o[w][r][d], acc);
-      lsum = fmaf(wt, sm_l[w][r], lsum);
+    for (int si = 0; si < kSplitSteps; ++si) {
+      if (si == kMidStep) {
+        lds_barrier();  // split k + 1 published
+        int n_hg;
+        load_desc(sh.desc[(k + 1) % kQueue], n_valid, n_tb, n_te, n_tlo, n_page0, n_pages, n_hg);
+        n_lane_off = sh.desc[(k + 1) % kQueue].loff[lane];
+      }
+      // step si + kAhead of this split, or one of the next split's first steps, into the
+      // slot the previous step was consumed from
+      const int ahead = si + kAhead;
+      if (ahead < kSplitSteps)
+        issue(c_valid, c_tb, c_te, c_tlo, c_page0, c_pages, lane_off, ahead,
+              kr[ahead % kRing], vr[ahead % kRing]);
+      else
+        issue(n_valid, n_tb, n_te, n_tlo, n_page0, n_pages, n_lane_off, ahead - kSplitSteps,
+              kr[ahead % kRing], vr[ahead % kRing]);
+      consume(si, kr[si % kRing], vr[si % kRing]);
+      // keep the steps in program order: hoisting later steps' loads and address work
+      // into this one only lengthens register lifetimes
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const size_t slot = ((size_t)b * num_q_heads + hh) * max_splits + split;
-    ws_o[slot * D + d] = acc;
-    if (d == 0) {
-      ws_ml[slot * 2] = big;
-      ws_ml[slot * 2 + 1] = lsum;
+    // end of split k: its state per head for the scheduler's merge
+    const int buf = k & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sh.mo[buf][wave][row][col * 8 + i] = o[i];
+    if (col == 0) {
+      sh.mm[buf][wave][row] = m;
+      sh.ml[buf][wave][row] = l;
     }
+    lds_barrier();
+    if (!n_valid) break;
+    c_valid = n_valid;
+    c_tb = n_tb;
+    c_te = n_te;
+    c_tlo = n_tlo;
+    c_page0 = n_page0;
+    c_pages = n_pages;
+    lane_off = n_lane_off;
+    load_query(sh.desc[(k + 1) % kQueue]);
+    m = kEmptyMax;
+    l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = 0.f;
   }
+  // the loads issued ahead for a split that does not exist read nothing; let them
+  // retire before the wave ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // One wave per (sequence, head), four heads per workgroup: the wave walks the splits
@@ -318,21 +490,36 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
   for (int e = 0; e < kPerLane; ++e) dst[e] = to_bf16_bits(acc[e] * inv);
 }
 
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D>
 void launch_partial(const DecodeArgs& a, hipStream_t stream) {
-  using G = DecodeGeometry<D>;
-  const dim3 grid((a.num_q_heads + G::kHeads - 1) / G::kHeads, decode_grid_splits(a), a.batch);
-  hipLaunchKernelGGL(decode_partial_kernel<D>, grid, dim3(kThreads), 0, stream, a.q, a.k_pool,
-                     a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
-                     score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
-                     a.log2_page_size, a.max_pages_per_seq, a.split_tokens, a.max_splits,
-                     a.window);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
+                     a.batch, a.split_tokens, a.max_splits, a.window, a.plan);
+  hipLaunchKernelGGL(decode_partial_kernel<D>, dim3(cu_count()), dim3(kThreads), 0, stream,
+                     a.q, a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
+                     a.plan, score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
+                     a.log2_page_size, a.max_pages_per_seq, a.max_splits, a.window);
 }
 
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   if (decode_grouped(a)) return launch_decode_partial_gqa(a, stream);
+  // one-head-per-row splits are kSplitTokensMha keys (pages hold at most 256 tokens)
+  if (a.split_tokens != kSplitTokensMha) return hipErrorInvalidValue;
   if (a.head_dim == 128) launch_partial<128>(a, stream);
   else launch_partial<64>(a, stream);
   return hipGetLastError();

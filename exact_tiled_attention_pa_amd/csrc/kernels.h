@@ -37,6 +37,7 @@ struct DecodeArgs {
   uint16_t* out;
   float* ws_o;        // [batch, num_q_heads, max_splits, head_dim]
   float* ws_ml;       // [batch, num_q_heads, max_splits, 2]  (m in log2 units, l)
+  int32_t* plan;      // [2 + batch * max_splits]: claim counter, pair count, pairs
   float scale;
   int batch;
   int num_q_heads;
@@ -56,23 +57,22 @@ inline bool decode_grouped(const DecodeArgs& a) {
   return a.num_q_heads / a.num_kv_heads >= kGqaMinGroup;
 }
 
-// Splits of a windowed one-head-per-row decode: they start at the window's first key
-// rounded down to a multiple of 4 and the last one runs to the sequence end, so a
-// window of w keys takes ceil(min(w, L) / split_tokens) splits (decode.hip).
+// Splits of a windowed one-head-per-row decode: laid back from the sequence end, so a
+// window of w keys takes ceil(min(w, L) / split_tokens) of them (decode.hip).
 __host__ __device__ inline int window_split_count(int seq_len, int window, int split_tokens) {
   const int w = seq_len < window ? seq_len : window;
   return w > 0 ? (w + split_tokens - 1) / split_tokens : 0;
 }
 
-// Decode grids.  Without a window row y is split y.  With a sliding window only the
-// splits that can hold keys inside it are launched: the one-head-per-row decode walks
-// the window-aligned splits above; the grouped-head decode keeps the splits at
-// multiples of split_tokens and counts back from each sequence's last split (a window
-// of w keys touches at most ceil(w / split_tokens) + 1 of them), grid row y walking
-// split (L_b - 1) / split_tokens - y (decode_split_of).
+// Grid rows of the grouped-head decode (decode_gqa.hip).  Without a window row y is
+// split y.  With a sliding window only the splits that can hold keys inside it are
+// launched: the splits stay at multiples of split_tokens and the rows count back from
+// each sequence's last split (a window of w keys touches at most ceil(w / split_tokens)
+// + 1 of them), grid row y walking split (L_b - 1) / split_tokens - y (decode_split_of).
+// The one-head-per-row decode takes its work from a list instead (decode.hip).
 inline int decode_grid_splits(const DecodeArgs& a) {
   if (a.window <= 0) return a.max_splits;
-  const int n = (a.window + a.split_tokens - 1) / a.split_tokens + (decode_grouped(a) ? 1 : 0);
+  const int n = (a.window + a.split_tokens - 1) / a.split_tokens + 1;
   return n < a.max_splits ? n : a.max_splits;
 }
 

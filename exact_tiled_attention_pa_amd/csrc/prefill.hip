@@ -301,15 +301,30 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_po
   };
   auto finish_tile = [&](int j) {
     const int kt0 = j * BN;
-    // mask: register r of block kb holds key kt0 + 32kb + 8(r/4) + 4*half + r%4
-    if (j >= full_tiles || j < window_masked_tiles) {
+    // mask: register r of block kb holds key kt0 + 4*half + c with the constant
+    // c = 32kb + 8(r/4) + r%4 (0..59), so each bound is one compare of c against a
+    // per-lane threshold: keys past the row's last visible key (tiles crossing the
+    // diagonal or the sequence end), and keys before its window (tiles crossing the
+    // window's lower edge)
+    if (j >= full_tiles) {
       const int lim = CAUSAL ? min(my_pos, seq_len - 1) : seq_len - 1;
+      const int hi = lim - kt0 - half * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          sacc[kb][r] = (key <= lim && key >= my_lo) ? sacc[kb][r] : -INFINITY;
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          sacc[kb][r] = c <= hi ? sacc[kb][r] : -INFINITY;
+        }
+    }
+    if (j < window_masked_tiles) {
+      const int lo = my_lo - kt0 - half * 4;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          sacc[kb][r] = c >= lo ? sacc[kb][r] : -INFINITY;
         }
     }
 

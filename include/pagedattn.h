@@ -120,8 +120,9 @@ int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
 
 /*
  * Bytes of device workspace pa_decode needs for `batch` sequences: per
- * (sequence, query head, split) one partial (m, l, O[head_dim]) in fp32.
- * Returns 0 for invalid arguments.
+ * (sequence, query head, split) one partial (m, l, O[head_dim]) in fp32, plus
+ * the first pass's work list (a counter, a count and one 32-bit entry per
+ * (sequence, split)).  Returns 0 for invalid arguments.
  */
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                  const pa_kv_layout* layout);

@@ -114,7 +114,8 @@ def test_decode_workspace_size_formula(lib):
     o = 64 * 32 * 32 * 128 * 4
     ml = 64 * 32 * 32 * 2 * 4
     r = lambda n: (n + 255) // 256 * 256
-    assert lib.pa_decode_workspace_bytes(64, 32, ctypes.byref(layout)) == r(o) + r(ml)
+    plan = (2 + 64 * 32) * 4  # claim counter, pair count, (sequence, split) pairs
+    assert lib.pa_decode_workspace_bytes(64, 32, ctypes.byref(layout)) == r(o) + r(ml) + r(plan)
     big = B.make_layout(128, 256, 8, 128, 128)
     assert lib.pa_decode_split_tokens(8, ctypes.byref(big)) == 256
     bad = B.make_layout(128, 24, 8, 128, 128)
@@ -128,7 +129,8 @@ def test_decode_workspace_size_formula(lib):
     assert lib.pa_decode_split_tokens(12, ctypes.byref(gl)) == 0  # not a multiple of 8
     o = 64 * 64 * 8 * 128 * 4
     ml = 64 * 64 * 8 * 2 * 4
-    assert lib.pa_decode_workspace_bytes(64, 64, ctypes.byref(gl)) == r(o) + r(ml)
+    plan = (2 + 64 * 8) * 4
+    assert lib.pa_decode_workspace_bytes(64, 64, ctypes.byref(gl)) == r(o) + r(ml) + r(plan)
 
 
 def test_decode_rejects(lib):

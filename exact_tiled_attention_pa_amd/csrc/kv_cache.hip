@@ -11,8 +11,10 @@
 // only when their contents diverge).
 //
 // Both are plain byte movers bound by HBM bandwidth: one workgroup per token (or per
-// page), 16-byte vector loads and stores, coalesced along the contiguous token row
-// (all heads of a token are adjacent in the [page, slot, head, d] layout).  Entries
+// 16 KB piece of a page pair), 16-byte vector loads and stores, coalesced along the
+// contiguous token row (all heads of a token are adjacent in the [page, slot, head, d]
+// layout); the page copy issues all of a piece's loads before its stores, both
+// non-temporal.  Entries
 // whose sequence id, position, table entry or page id fall outside the given ranges
 // are skipped, so a bad index can never write outside the pools.
 
@@ -60,9 +62,25 @@ copy_pages_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
   const char* vs = reinterpret_cast<const char*>(v_pool) + (size_t)s * page_bytes;
   char* kd = reinterpret_cast<char*>(k_pool) + (size_t)d * page_bytes;
   char* vd = reinterpret_cast<char*>(v_pool) + (size_t)d * page_bytes;
-  for (size_t o = begin + threadIdx.x * 16; o < end; o += kThreads * 16) {
-    *reinterpret_cast<u32x4*>(kd + o) = *reinterpret_cast<const u32x4*>(ks + o);
-    *reinterpret_cast<u32x4*>(vd + o) = *reinterpret_cast<const u32x4*>(vs + o);
+  // every load of the piece before any store, both non-temporal (each byte is moved
+  // once): 5.27 against 4.91 TB/s for load-store pairs with ordinary caching
+  constexpr int kPer = kPiece / (kThreads * 16);
+  u32x4 kv[kPer], vv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const size_t o = begin + (size_t)(i * kThreads + threadIdx.x) * 16;
+    if (o < end) {
+      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + o));
+      vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + o));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const size_t o = begin + (size_t)(i * kThreads + threadIdx.x) * 16;
+    if (o < end) {
+      __builtin_nontemporal_store(kv[i], reinterpret_cast<u32x4*>(kd + o));
+      __builtin_nontemporal_store(vv[i], reinterpret_cast<u32x4*>(vd + o));
+    }
   }
 }
 

@@ -34,3 +34,49 @@ def test_repeated_calls_are_bitwise_identical(name):
         del scratch
     del wl, firsts
     torch.cuda.empty_cache()
+
+
+def test_concurrent_decodes_on_two_streams():
+    """The first decode pass claims its work from a counter in the call's own workspace,
+    so two decodes with their own workspaces running at the same time on two streams
+    (here a short-sequence batch and a long-sequence batch, each with and without a
+    window) give exactly what each gives alone."""
+    from exact_tiled_attention_pa_amd import binding as B
+
+    G.banner("two decodes on two streams")
+    wa = W.build("conc_a", 81, heads=8, head_dim=128, page_size=16,
+                 lens=[int(x) for x in torch.randint(1, 3000, (48,), generator=torch.Generator().manual_seed(81))],
+                 kind="decode", pool_slack=1.2, device="cuda")
+    wb = W.build("conc_b", 82, heads=4, head_dim=64, page_size=64, lens=[20000, 9000, 131, 47000],
+                 kind="decode", pool_slack=1.2, device="cuda")
+    ca, cb = wa.calls[0], wb.calls[0]
+    for window in (0, 700):
+        alone = []
+        for wl, c in ((wa, ca), (wb, cb)):
+            out = torch.empty_like(c.q)
+            ws = B.decode_workspace(c.q, wl.k_pool, c.block_table)
+            B.pa_decode(c.q, wl.k_pool, wl.v_pool, c.block_table, c.seq_lens, wl.scale, out, ws,
+                        window=window)
+            torch.cuda.synchronize()
+            alone.append(out)
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        ws_a = B.decode_workspace(ca.q, wa.k_pool, ca.block_table)
+        ws_b = B.decode_workspace(cb.q, wb.k_pool, cb.block_table)
+        out_a = torch.full_like(ca.q, float("nan"))
+        out_b = torch.full_like(cb.q, float("nan"))
+        torch.cuda.synchronize()
+        for _ in range(3):
+            fork = torch.cuda.Event()
+            fork.record(main)
+            side.wait_event(fork)
+            B.pa_decode(ca.q, wa.k_pool, wa.v_pool, ca.block_table, ca.seq_lens, wa.scale, out_a,
+                        ws_a, window=window, stream=side)
+            B.pa_decode(cb.q, wb.k_pool, wb.v_pool, cb.block_table, cb.seq_lens, wb.scale, out_b,
+                        ws_b, window=window)
+            join = torch.cuda.Event()
+            join.record(side)
+            main.wait_event(join)
+            torch.cuda.synchronize()
+            assert torch.equal(out_a, alone[0]), f"batch a, window {window}"
+            assert torch.equal(out_b, alone[1]), f"batch b, window {window}"

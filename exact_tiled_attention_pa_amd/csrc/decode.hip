@@ -37,6 +37,8 @@
 // Query head h reads K/V head h / (num_q_heads / num_kv_heads).  m is kept in
 // log2 units (scores times scale * log2(e)) so every exponential is one v_exp_f32.
 
+#include <atomic>
+
 #include "device_util.h"
 #include "kernels.h"
 #include "lds_tile.h"
@@ -490,18 +492,21 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
   for (int e = 0; e < kPerLane; ++e) dst[e] = to_bf16_bits(acc[e] * inv);
 }
 
+// Compute units of the current device, looked up once per device (pass 1 runs one
+// persistent workgroup per CU).  Calls from several host threads may race to fill an
+// entry; they store the same value.
 int cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int D>

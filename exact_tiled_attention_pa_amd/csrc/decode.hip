@@ -54,7 +54,7 @@ constexpr int kRing = 2;                     // register slots per streaming wav
 constexpr int kAhead = kRing - 1;            // steps in flight ahead of the one consumed
 constexpr int kQueue = 4;                    // split descriptors held in LDS
 constexpr int kItemPages = 32;               // pages one split may touch (<= 17 here)
-constexpr int kSplitTokensMha = 256;         // keys per split (kDecodeSplitTokens)
+constexpr int kSplitTokensMha = kDecodeSplitTokens;  // keys per split
 constexpr int kSplitSteps = kSplitTokensMha / kChunk;  // 8 steps of 32 keys
 constexpr int kMidStep = 4;                  // step at which the next split is published
 static_assert(kSplitSteps % kRing == 0, "every split starts in ring slot 0");

@@ -44,6 +44,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 32;               // keys per tile
 constexpr int kHeadBlock = 32;          // query heads per workgroup (MFMA columns)
 constexpr int kRescaleThreshold = 8;    // log2 units a row max may grow before rescaling
+// cache policy of the K/V loads: non-temporal, every byte is read once (227.5 -> 206.3 us
+// on a 64-sequence, 8-K/V-head decode against the default policy, same box)
+constexpr int kNonTemporal = 2;
 
 template <int D>
 struct GqaGeometry {
@@ -182,10 +185,10 @@ decode_gqa_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       const int voff = v_voff[i % G::kInstPerGroup];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(k_pool + elem, bytes),
                                                (lds_void*)(k_lds + first_row * G::kRowBytes),
-                                               16, koff, 0, 0, 0);
+                                               16, koff, 0, 0, kNonTemporal);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(v_pool + elem, bytes),
                                                (lds_void*)(v_lds + first_row * G::kRowBytes),
-                                               16, voff, 0, 0, 0);
+                                               16, voff, 0, 0, kNonTemporal);
     }
   };
 

@@ -23,9 +23,9 @@ on the stream the library launches on (torch's current stream):
 Each kernel's rate uses its average event-timed launch (the figure rocprofv3's
 average duration is compared with); median and minimum are reported beside it.
 `input_sha256` holds a digest of every input buffer of every workload.
-`cpu_baseline` times the CPU oracle over a pool of host processes on decode_64 and on
-query rows of the two causal prefills, and compares the oracle's outputs with the
-GPU outputs of the timed runs (`parity`).
+`cpu_baseline` times the CPU oracle over a pool of host processes on every workload
+(whole decode sequences; all or every 2nd / 8th query row of the prefills and chunks)
+and compares the oracle's outputs with the GPU outputs of the timed runs (`parity`).
 
 Usage: python bench.py [--steps K] [--warmup W] [--legs a,b,...] [--no-cpu-baseline]
        [--no-digest]
@@ -485,10 +485,10 @@ def _oracle_task(task):
         res = out[sel]
     else:
         q_start = _worker_arrays(paths)[5]
-        b = meta["seq"]
+        b, rows = sel
         out, _ = OA.paged_prefill(q, k, v, table, lens, q_start, meta["causal"], meta["scale"],
-                                  rows={b: sel})
-        res = out[int(q_start[b]) + sel]
+                                  rows={b: rows})
+        res = out[int(q_start[b]) + rows]
     return res, time.perf_counter() - t0
 
 
@@ -564,11 +564,11 @@ def cpu_baseline(legs, scratch_dir):
                 np.save(p, a)
                 paths.append(p)
             del arrays
-            meta = {"scale": wl.scale, "causal": call.causal, "seq": 0}
+            meta = {"scale": wl.scale, "causal": call.causal}
             if call.kind == "decode":
                 tasks = [("decode", paths, meta, [int(b)]) for b in sample]
             else:
-                tasks = [("prefill", paths, meta, rows) for rows in sample]
+                tasks = [("prefill", paths, meta, piece) for piece in sample]
             t0 = time.perf_counter()
             results = pool.map(_oracle_task, tasks, chunksize=1)
             wall = time.perf_counter() - t0
@@ -584,14 +584,19 @@ def cpu_baseline(legs, scratch_dir):
                         f"tokens, all {wl.num_q_heads} query heads)")
             else:
                 ref = np.concatenate([r for r, _ in results])
-                rows = np.concatenate(sample)
-                rows_bits = got[int(call.q_start_host[0]) + rows]
-                L, q_len = int(call.seq_lens_host[0]), int(call.q_start_host[1])
-                pos = L - q_len + rows
-                pairs = int(np.minimum(pos + 1, L).sum()) if call.causal else L * len(rows)
+                qs = call.q_start_host
+                rows_bits = got[np.concatenate([int(qs[b]) + rows for b, rows in sample])]
+                pairs = n_rows = 0
+                for b, rows in sample:
+                    L, q_len = int(call.seq_lens_host[b]), int(qs[b + 1] - qs[b])
+                    pos = L - q_len + rows
+                    pairs += int(np.minimum(pos + 1, L).sum()) if call.causal else L * len(rows)
+                    n_rows += len(rows)
                 work = 4 * wl.head_dim * wl.num_q_heads * pairs
                 rate, unit = work / wall / 1e12, "TFLOP/s"
-                what = (f"{len(rows)} of {q_len} query rows spread over the sequence, all "
+                n_seqs = len({b for b, _ in sample})
+                what = (f"{n_rows} of {int(qs[-1])} query rows spread over "
+                        f"{n_seqs} sequence{'s' if n_seqs > 1 else ''}, all "
                         f"{wl.num_q_heads} heads ({pairs} visible pairs per head)")
             entries[name] = {"value": round(rate, 6), "unit": unit, "wall_s": round(wall, 2),
                              "cpu_s": round(sum(t for _, t in results), 2), "sample": what,
@@ -609,17 +614,25 @@ def cpu_baseline(legs, scratch_dir):
             "legs": entries}
 
 
+# every how-many-th query row of each sequence the oracle evaluates (1: all of them)
+BASELINE_ROW_STRIDE = {"prefill_32k": 8, "mixed_128x4_chunks": 8, "prefill_4096_noncausal": 2}
+
+
 def baseline_samples(name, wl, call):
-    """What the oracle evaluates for each leg: whole decode sequences, or query rows
-    (every row-stride-th row, from an offset) split into tasks."""
+    """What the oracle evaluates for each leg: whole decode sequences, or (sequence,
+    query rows) tasks of up to 32 rows, every row-stride-th row of each sequence from an
+    offset."""
     import numpy as np
     if call.kind == "decode":
         return list(range(call.batch))
-    q_len = int(call.q_start_host[1])
-    stride = {"prefill_32k": 8}.get(name, 1)
-    rows = np.arange(stride // 2, q_len, stride, dtype=np.int64)
+    stride = BASELINE_ROW_STRIDE.get(name, 1)
     per_task = 32
-    return [rows[i:i + per_task] for i in range(0, len(rows), per_task)]
+    tasks = []
+    for b in range(call.batch):
+        q_len = int(call.q_start_host[b + 1] - call.q_start_host[b])
+        rows = np.arange(stride // 2, q_len, stride, dtype=np.int64)
+        tasks += [(b, rows[i:i + per_task]) for i in range(0, len(rows), per_task)]
+    return tasks
 
 
 # ------------------------------------------------------------------ rocprofv3 summaries
@@ -730,7 +743,10 @@ def summarize_mfma(pmc_dir, kind, workload, out_path, command):
 
 LEGS = ("decode_64", "prefill_4096_causal", "prefill_4096_noncausal", "prefill_32k",
         "mixed_128x4", "prefill_600", "next")
-BASELINE_LEGS = ("decode_64", "prefill_4096_causal", "prefill_32k")
+# the oracle's legs, in the order they run; the mixed batch gives two (its decode call
+# and its chunk prefill)
+BASELINE_LEGS = ("decode_64", "prefill_4096_causal", "prefill_4096_noncausal", "prefill_32k",
+                 "mixed_128x4_decode", "mixed_128x4_chunks", "prefill_600")
 
 
 def main():
@@ -827,7 +843,8 @@ def main():
             })
         elif leg == "mixed_128x4":
             res, (dout, pout) = mixed_leg(wl, args.steps, max(args.warmup, 10))
-            kept[leg] = (wl, wl.calls[1], pout)
+            kept["mixed_128x4_decode"] = (wl, wl.calls[0], dout)
+            kept["mixed_128x4_chunks"] = (wl, wl.calls[1], pout)
             result["mixed"] = res
         else:
             res, out = prefill_leg(wl, wl.calls[0], args.steps,
@@ -869,7 +886,7 @@ def main():
     # the oracle runs last, after every GPU leg, so its host time cannot idle the GPU
     # between a warm-up and a timed region
     if not args.no_cpu_baseline:
-        todo = {k: v for k, v in kept.items() if k in BASELINE_LEGS}
+        todo = {k: kept[k] for k in BASELINE_LEGS if k in kept}
         if todo:
             import shutil
             import tempfile

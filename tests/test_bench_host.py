@@ -138,8 +138,11 @@ def test_cpu_baseline_pool_on_small_workloads(tmp_path, monkeypatch):
                   kind="decode", pool_slack=1.3, device="cpu", q_heads=4)
     pre = W.build("prefill_32k", 6, heads=2, head_dim=64, page_size=16, lens=[200],
                   q_lens=[200], causal=True, device="cpu")
+    # chunks on cached context, as in the mixed batch: 3 sequences, rows not starting at 0
+    chunks = W.build("mixed_128x4", 7, heads=2, head_dim=64, page_size=16,
+                     lens=[150, 90, 260], q_lens=[40, 90, 33], causal=True, device="cpu")
     legs = {}
-    for name, wl in (("decode_64", dec), ("prefill_32k", pre)):
+    for name, wl in (("decode_64", dec), ("prefill_32k", pre), ("mixed_128x4_chunks", chunks)):
         call = wl.calls[0]
         q = W.to_host_bits(call.q)
         k, v = W.to_host_bits(wl.k_pool), W.to_host_bits(wl.v_pool)
@@ -160,6 +163,17 @@ def test_cpu_baseline_pool_on_small_workloads(tmp_path, monkeypatch):
         assert leg["parity"]["max_abs"] <= 1e-2
     # the prefill sample: every 8th row from row 4, all heads
     assert p["parity"]["elements"] == len(range(4, 200, 8)) * 2 * 64
+    # the chunk sample: every 8th row of each sequence from its row 4; its visible pairs
+    # counted by brute force over the sampled rows' absolute positions
+    c = res["legs"]["mixed_128x4_chunks"]
+    assert c["parity"]["within_tolerance"], c
+    lens, q_lens = [150, 90, 260], [40, 90, 33]
+    rows = [range(4, n, 8) for n in q_lens]
+    assert c["parity"]["elements"] == sum(len(r) for r in rows) * 2 * 64
+    pairs = sum(1 for L, n, rr in zip(lens, q_lens, rows) for i in rr for t in range(L)
+                if t <= L - n + i)
+    assert f"({pairs} visible pairs per head)" in c["sample"]
+    assert "over 3 sequences" in c["sample"]
     assert os.listdir(tmp_path) == []
 
 

@@ -162,11 +162,29 @@ def decode_kind(wl) -> str:
     return "decode_gqa" if wl.num_q_heads // wl.heads >= GQA_MIN_GROUP else "decode"
 
 
-def prefill_kernel_name(wl, causal) -> str:
-    """The prefill instantiation a workload runs: head dim, causal, and whether a key tile
-    of 64 lies in one page (pages of 64 tokens or more)."""
-    return (f"prefill_kernel<{wl.head_dim}, {str(bool(causal)).lower()}, "
-            f"{str(wl.page_size >= 64).lower()}>")
+# the library's choice between its two prefill kernels (prefill_split.h): the split-key
+# kernel when its grid of 32-row workgroups fits one per CU and a sequence may span more
+# than one 64-key tile, unless PA_PREFILL_PATH forces one
+PREFILL_SPLIT_BLOCK_M = 32
+PREFILL_SPLIT_MAX_WORKGROUPS = 256
+
+
+def prefill_takes_split(wl, call) -> bool:
+    path = os.environ.get("PA_PREFILL_PATH", "") or "auto"
+    if path != "auto":
+        return path == "split"
+    wgs = wl.num_q_heads * call.batch * (-(-call.max_q_len // PREFILL_SPLIT_BLOCK_M))
+    return (wgs <= PREFILL_SPLIT_MAX_WORKGROUPS and
+            int(call.block_table.shape[1]) * wl.page_size > 64)
+
+
+def prefill_kernel_name(wl, call) -> str:
+    """The prefill instantiation a call runs: which kernel, head dim, causal and, for the
+    tiled kernel, whether a key tile of 64 lies in one page (pages of 64 tokens or more)."""
+    causal = str(bool(call.causal)).lower()
+    if prefill_takes_split(wl, call):
+        return f"prefill_split_kernel<{wl.head_dim}, {causal}>"
+    return f"prefill_kernel<{wl.head_dim}, {causal}, {str(wl.page_size >= 64).lower()}>"
 
 
 def decode_kernel_name(wl) -> str:
@@ -324,14 +342,14 @@ def prefill_leg(wl, call, steps, warmup):
     from exact_tiled_attention_pa_amd import binding as B
     flops, nbytes = prefill_work(wl, call)
     out = torch.empty_like(call.q)
-
-    def run():
-        B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
-                     call.causal, wl.scale, out, call.q_start, call.max_q_len)
+    # validated and marshalled once: each timed launch is one C call, so short launches
+    # (the 600-token example) are not paced by the binding's per-call checks
+    run = B.PreparedPrefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
+                            call.causal, wl.scale, out, call.q_start, call.max_q_len).launch
 
     wall, tm = timed_launches(run, steps, warmup, warm_s=PREFILL_WARM_S)
     roof = _rate(flops, tm, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
-                 kernel=prefill_kernel_name(wl, call.causal))
+                 kernel=prefill_kernel_name(wl, call))
     wl_key = wl.name if len(wl.calls) == 1 else f"{wl.name}_chunks"
     roof.update(traffic=recorded_traffic("prefill", wl_key),
                 mfma_busy=recorded_mfma("prefill", wl_key))
@@ -441,7 +459,7 @@ def next_rows_summary(decode_wl, steps, warmup):
     flops = 4 * p.head_dim * pc.q.shape[1] * pairs
     res["window_prefill"] = _rate(flops, tm, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", bound="mfma",
                                   workload=f"prefill_32k, window {w}",
-                                  kernel=prefill_kernel_name(p, True))
+                                  kernel=prefill_kernel_name(p, pc))
     del p, pc, out
     torch.cuda.empty_cache()
     return res

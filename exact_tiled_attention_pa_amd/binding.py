@@ -260,12 +260,10 @@ def _check_device_tensors(**tensors):
         _require(t.device == dev, f"{name} is on {t.device}, expected {dev}")
 
 
-def pa_prefill(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_start,
-               max_q_len: int, stream=None, window: int = 0):
-    """Paged (chunked) prefill: out[q_start[b]:q_start[b+1]] = attention of sequence b's
-    query rows over its L_b = seq_lens[b] paged keys.  See pa_prefill in pagedattn.h;
-    window > 0 calls pa_prefill_window.  With the contract check on, the block table,
-    lengths and chunk offsets are checked on the host first (ContractError)."""
+def _prefill_args(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_start,
+                  max_q_len, window):
+    """Validates a prefill call and returns (C function, its arguments but the stream,
+    the layout they point to)."""
     _enforce_contract(block_table, seq_lens, k_pool, q_start=q_start,
                       max_q_len=int(max_q_len), total_q=int(q.shape[0]))
     _check_device_tensors(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
@@ -281,18 +279,48 @@ def pa_prefill(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_s
     _require(block_table.dim() == 2 and block_table.shape[0] >= batch, "block_table: [batch, maxp]")
     _require(q_start.numel() == batch + 1, "q_start: [batch + 1]")
     lay = layout_of(k_pool, block_table)
-    if window:
-        st = load_library().pa_prefill_window(
-            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+    head = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
             int(bool(causal)), float(scale), _ptr(out), _ptr(q_start), batch, q.shape[1],
-            int(max_q_len), int(window), ctypes.byref(lay), _stream(stream))
-    else:
-        st = load_library().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-                                       _ptr(seq_lens), int(bool(causal)), float(scale),
-                                       _ptr(out), _ptr(q_start), batch, q.shape[1],
-                                       int(max_q_len), ctypes.byref(lay), _stream(stream))
-    _check(st)
+            int(max_q_len))
+    lib = load_library()
+    if window:
+        return lib.pa_prefill_window, head + (int(window), ctypes.byref(lay)), lay
+    return lib.pa_prefill, head + (ctypes.byref(lay),), lay
+
+
+def pa_prefill(q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_start,
+               max_q_len: int, stream=None, window: int = 0):
+    """Paged (chunked) prefill: out[q_start[b]:q_start[b+1]] = attention of sequence b's
+    query rows over its L_b = seq_lens[b] paged keys.  See pa_prefill in pagedattn.h;
+    window > 0 calls pa_prefill_window.  With the contract check on, the block table,
+    lengths and chunk offsets are checked on the host first (ContractError)."""
+    fn, args, _lay = _prefill_args(q, k_pool, v_pool, block_table, seq_lens, causal, scale,
+                                   out, q_start, max_q_len, window)
+    _check(fn(*args, _stream(stream)))
     return out
+
+
+class PreparedPrefill:
+    """A pa_prefill call validated and marshalled once, then launched any number of times
+    on the same buffers (whose contents may change between launches): each launch is one
+    C call, so a serving loop or a short prefill pays the checks once instead of per
+    launch.  With the contract check on, it runs when the call is prepared.  The object
+    keeps its tensors alive."""
+
+    def __init__(self, q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_start,
+                 max_q_len: int, window: int = 0):
+        self._fn, self._args, self._lay = _prefill_args(
+            q, k_pool, v_pool, block_table, seq_lens, causal, scale, out, q_start, max_q_len,
+            window)
+        self._tensors = (q, k_pool, v_pool, block_table, seq_lens, out, q_start)
+        self.out = out
+
+    def launch(self, stream=None):
+        """Enqueues the prefill on `stream` (default: torch's current stream); returns out."""
+        st = self._fn(*self._args, _stream(stream))
+        if st != PA_OK:
+            raise PagedAttnError(st, last_error())
+        return self.out
 
 
 def pa_decode_workspace_bytes(batch: int, num_q_heads: int, layout: KVLayout) -> int:

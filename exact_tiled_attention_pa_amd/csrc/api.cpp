@@ -8,8 +8,11 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "kernels.h"
+#include "prefill_split.h"
 #include "status.h"
 
 namespace {
@@ -188,6 +191,16 @@ pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf1
   return a;
 }
 
+// PA_PREFILL_PATH: unset, empty or "auto" lets the launch size choose the prefill
+// kernel; "tiles" or "split" forces one (tests run both at every shape).  -1: unknown.
+int prefill_path_from_env() {
+  const char* s = std::getenv("PA_PREFILL_PATH");
+  if (!s || !*s || !std::strcmp(s, "auto")) return pa::kPrefillPathAuto;
+  if (!std::strcmp(s, "tiles")) return pa::kPrefillPathTiles;
+  if (!std::strcmp(s, "split")) return pa::kPrefillPathSplit;
+  return -1;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
@@ -226,6 +239,10 @@ int pa_prefill_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_
     return fail(PA_ERR_NULL, "every array argument of pa_prefill must be non-NULL");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return fail(PA_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+  const int path = prefill_path_from_env();
+  if (path < 0)
+    return fail(PA_ERR_INVALID_ARG, "PA_PREFILL_PATH=%s: expected auto, tiles or split",
+                std::getenv("PA_PREFILL_PATH"));
   if (batch == 0 || max_q_len == 0) return ok();
 
   pa::PrefillArgs a;
@@ -246,6 +263,12 @@ int pa_prefill_window(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_
   a.max_pages_per_seq = layout->max_pages_per_seq;
   a.max_q_len = max_q_len;
   a.window = window;
+  if (pa::prefill_takes_split(a, path)) {
+    if ((max_q_len + pa::kPrefillSplitBlockM - 1) / pa::kPrefillSplitBlockM > 65535)
+      return fail(PA_ERR_INVALID_ARG,
+                  "max_q_len=%d needs more than 65535 split-key query tiles", max_q_len);
+    return hip_status(pa::launch_prefill_split(a, stream), "split-key prefill launch");
+  }
   return hip_status(pa::launch_prefill(a, stream), "prefill launch");
 }
 

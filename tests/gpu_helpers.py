@@ -30,6 +30,16 @@ def banner(msg: str):
     print(f"[case] {msg}", flush=True)
 
 
+@pytest.fixture(params=["tiles", "split"])
+def prefill_path(request, monkeypatch):
+    """Runs a prefill test once with each prefill kernel forced through PA_PREFILL_PATH:
+    the 128-row tiled kernel and the split-key kernel (which small launches take by
+    default)."""
+    monkeypatch.setenv("PA_PREFILL_PATH", request.param)
+    print(f"[case] prefill path {request.param}", flush=True)
+    return request.param
+
+
 def run_call(wl: W.Workload, call: W.AttnCall, out=None, workspace=None):
     """Runs one library call of a workload on the current stream; returns out (bf16)."""
     if out is None:

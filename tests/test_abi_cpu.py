@@ -197,6 +197,8 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         B.pa_prefill(q, q, q, q, q, True, 0.1, q, q, 4)
+    with pytest.raises(ValueError):  # a prepared call runs the same checks, once
+        B.PreparedPrefill(q, q, q, q, q, True, 0.1, q, q, 4)
 
 
 def test_kv_append_rejects(lib):
@@ -232,3 +234,20 @@ def test_copy_pages_rejects(lib):
     assert call(layout=B.make_layout(4, 256, 8192, 128, 1)) == B.PA_ERR_INVALID_ARG
     assert call(k=FAKE + 8) == B.PA_ERR_INVALID_ARG
     assert call(n=0) == B.PA_OK
+
+
+def test_prefill_path_override_is_checked(lib, monkeypatch):
+    """PA_PREFILL_PATH forces one of the two prefill kernels; an unknown value is an
+    argument error before anything is enqueued (also for an empty batch), and a forced
+    split-key launch whose 32-row query tiles overflow the grid is refused."""
+    monkeypatch.setenv("PA_PREFILL_PATH", "fastest")
+    assert prefill(lib, lay()) == B.PA_ERR_INVALID_ARG
+    assert "PA_PREFILL_PATH=fastest" in B.last_error()
+    assert prefill(lib, lay(), batch=0) == B.PA_ERR_INVALID_ARG
+    for ok in ("", "auto", "tiles", "split"):
+        monkeypatch.setenv("PA_PREFILL_PATH", ok)
+        assert prefill(lib, lay(), batch=0) == B.PA_OK, ok
+    big = lay(num_pages=8700, ps=256, maxp=8700)
+    monkeypatch.setenv("PA_PREFILL_PATH", "split")
+    assert prefill(lib, big, max_q_len=32 * 65535 + 1) == B.PA_ERR_INVALID_ARG
+    assert "split-key" in B.last_error()

@@ -72,6 +72,23 @@ def test_gqa_threshold_matches_the_library():
     assert int(re.search(r"kGqaMinGroup\s*=\s*(\d+)", text).group(1)) == bench.GQA_MIN_GROUP
 
 
+def test_prefill_kernel_choice_matches_the_library():
+    """bench.py names the prefill kernel a call runs by the library's own rule: its
+    constants are the header's, and the worked example takes the split-key kernel
+    while the N=4096 workload takes the tiled one."""
+    import re
+    text = open(bench.os.path.join(bench.CSRC, "prefill_split.h")).read()
+    assert int(re.search(r"kPrefillSplitBlockM\s*=\s*(\d+)", text).group(1)) == \
+        bench.PREFILL_SPLIT_BLOCK_M
+    assert int(re.search(r"kPrefillSplitMaxWorkgroups\s*=\s*(\d+)", text).group(1)) == \
+        bench.PREFILL_SPLIT_MAX_WORKGROUPS
+    from exact_tiled_attention_pa_amd import workloads as W
+    small = W.prefill_600(tensors=False)
+    large = W.prefill_4096(causal=True, tensors=False)
+    assert bench.prefill_kernel_name(small, small.calls[0]) == "prefill_split_kernel<64, true>"
+    assert bench.prefill_kernel_name(large, large.calls[0]) == "prefill_kernel<128, true, true>"
+
+
 def test_kernel_source_lists_cover_local_includes():
     """The source hash that guards each counter summary covers every local header the
     kernel's file includes."""

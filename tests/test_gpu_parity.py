@@ -8,6 +8,7 @@ import torch
 from exact_tiled_attention_pa_amd import binding as B
 from exact_tiled_attention_pa_amd import workloads as W
 from tests import gpu_helpers as G
+from tests.gpu_helpers import prefill_path  # noqa: F401  (fixture)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +20,7 @@ def _gpu():
 
 # ----------------------------------------------------------------- small, element-wise
 
-def test_prefill_600_worked_example_full():
+def test_prefill_600_worked_example_full(prefill_path):
     """Paged causal prefill on the worked example's layout (600 tokens, pages of 256,
     table [5, 1, 9]); unread slots hold NaN.  Every output element is compared."""
     G.banner("prefill_600 full, poisoned pool")
@@ -44,7 +45,7 @@ PREFILL_CASES = [
 
 
 @pytest.mark.parametrize("d,ps,causal,hq,hkv,lens,q_lens", PREFILL_CASES)
-def test_prefill_small_element_wise(d, ps, causal, hq, hkv, lens, q_lens):
+def test_prefill_small_element_wise(d, ps, causal, hq, hkv, lens, q_lens, prefill_path):
     G.banner(f"prefill small d={d} ps={ps} causal={causal} Hq={hq} Hkv={hkv} lens={lens} "
              f"q_lens={q_lens}")
     wl = W.build("small", 100 + d + ps, heads=hkv, head_dim=d, page_size=ps, lens=lens,
@@ -316,7 +317,7 @@ def test_permuting_physical_pages_is_bitwise_invariant(which):
     assert torch.equal(base, out)
 
 
-def test_poisoned_and_clean_pools_agree_bitwise():
+def test_poisoned_and_clean_pools_agree_bitwise(prefill_path):
     """NaN in tail slots and unused pages must not change the output."""
     G.banner("poison vs clean, small prefill + decode")
     for kind in ("prefill", "decode"):
@@ -333,7 +334,7 @@ def test_poisoned_and_clean_pools_agree_bitwise():
         assert torch.equal(oa, ob), kind
 
 
-def test_constant_values_return_the_constant():
+def test_constant_values_return_the_constant(prefill_path):
     G.banner("constant V")
     for kind, hq in (("prefill", 2), ("decode", 2), ("decode", 16)):
         wl = W.build("c", 41, heads=2, head_dim=128, page_size=16, lens=[1, 500, 64],
@@ -398,7 +399,7 @@ WINDOW_PREFILL_CASES = [
 
 
 @pytest.mark.parametrize("d,ps,lens,q_lens,window", WINDOW_PREFILL_CASES)
-def test_prefill_sliding_window(d, ps, lens, q_lens, window):
+def test_prefill_sliding_window(d, ps, lens, q_lens, window, prefill_path):
     G.banner(f"prefill window={window} d={d} ps={ps} lens={lens} q_lens={q_lens}")
     wl = W.build("win", 300 + window, heads=3, head_dim=d, page_size=ps, lens=lens,
                  q_lens=q_lens, causal=True, pool_slack=1.3, device="cuda", poison=True)
@@ -449,7 +450,7 @@ def test_decode_window_split_alignment(window, ps):
               f"decode window={window} ps={ps}")
 
 
-def test_window_one_returns_own_value_row():
+def test_window_one_returns_own_value_row(prefill_path):
     """w = 1: every query sees only its own key, so O is exactly its own V row."""
     G.banner("window=1 exactness")
     wl = W.build("w1", 77, heads=2, head_dim=128, page_size=16, lens=[333], q_lens=[100],
@@ -468,7 +469,7 @@ def test_window_one_returns_own_value_row():
 # ----------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("causal,hq", [(True, 2), (False, 2), (True, 4)])
-def test_prefill_ragged_batch_with_empty_chunks(causal, hq):
+def test_prefill_ragged_batch_with_empty_chunks(causal, hq, prefill_path):
     """Sequences with no query rows in the middle of a batch, a one-row chunk on a long
     cache, a chunk that is the whole sequence: rows past each chunk are never written."""
     G.banner(f"prefill ragged batch with empty chunks causal={causal} Hq={hq}")
@@ -484,7 +485,7 @@ def test_prefill_ragged_batch_with_empty_chunks(causal, hq):
     G.compare(G.bf16_out_to_f64(out), ref, f"ragged causal={causal} Hq={hq}")
 
 
-def test_zero_scale_averages_the_visible_values():
+def test_zero_scale_averages_the_visible_values(prefill_path):
     """scale = 0: every visible key gets the same weight, so O is the mean of the
     visible V rows (causal prefill: a running mean; decode: the mean of the cache)."""
     G.banner("scale 0")
@@ -498,7 +499,7 @@ def test_zero_scale_averages_the_visible_values():
         G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), f"scale 0 {kind}")
 
 
-def test_prefill_window_grouped_heads():
+def test_prefill_window_grouped_heads(prefill_path):
     G.banner("prefill window=100 with 8 query heads over 2 K/V heads")
     wl = W.build("wg", 81, heads=2, head_dim=128, page_size=32, lens=[777, 300],
                  q_lens=[500, 300], causal=True, pool_slack=1.2, device="cuda", poison=True,
@@ -552,7 +553,7 @@ def test_grouped_decode_kernel_agrees_with_per_head_kernel():
 
 
 @pytest.mark.parametrize("hq", [4, 16])
-def test_decode_agrees_with_last_prefill_row(hq):
+def test_decode_agrees_with_last_prefill_row(hq, prefill_path):
     """Decode (split-K VALU or grouped MFMA kernel plus the combine pass) and the last row
     of a causal prefill (tiled MFMA kernel) over the same cache compute the same thing."""
     G.banner(f"decode vs last prefill row Hq={hq}")

@@ -14,6 +14,7 @@ from exact_tiled_attention_pa_amd import binding as B
 from exact_tiled_attention_pa_amd import workloads as W
 from oracle import attention as OA
 from tests import gpu_helpers as G
+from tests.gpu_helpers import prefill_path  # noqa: F401  (fixture)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +82,7 @@ def test_random_decode(seed):
 
 
 @pytest.mark.parametrize("seed", range(12))
-def test_random_prefill(seed):
+def test_random_prefill(seed, prefill_path):
     d, ps, hkv, hq, lens, q_lens, causal, window = prefill_case(seed)
     G.banner(f"random prefill seed={seed} d={d} ps={ps} Hkv={hkv} Hq={hq} lens={lens} "
              f"q_lens={q_lens} causal={causal} window={window}")
@@ -100,7 +101,7 @@ def test_random_prefill(seed):
     G.compare(G.bf16_out_to_f64(out), ref, f"random prefill seed={seed}")
 
 
-def test_many_short_sequences_decode_and_prefill():
+def test_many_short_sequences_decode_and_prefill(prefill_path):
     """Thousands of short decode sequences (grid z in the thousands, one chunk per
     split) and hundreds of short prefill chunks in one call."""
     rng = np.random.default_rng(77)

@@ -109,8 +109,18 @@ typedef struct pa_kv_layout {
  *   max_q_len    host-side upper bound of every q_len_b (sizes the grid without
  *                reading device memory); rows past q_len_b are never written
  * q, k_pool, v_pool and out must be 16-byte aligned (the kernels move 16-byte pieces).
+ * Two kernels compute the same attention: a tiled one (128 query rows per workgroup,
+ * their key tiles walked in order) and a split-key one for launches too small to fill
+ * the chip (32 query rows per workgroup whose four waves divide the key tiles and
+ * merge their softmax states).  The split-key kernel runs when
+ * num_q_heads * batch * ceil(max_q_len / 32) <= 256 and max_pages_per_seq * page_size
+ * > 64; the environment variable PA_PREFILL_PATH, read at each call, forces one
+ * ("tiles" or "split"; unset, empty or "auto": the rule above).  The two round
+ * differently, each within the same tolerance of the exact result.
  * Errors: PA_ERR_NULL, PA_ERR_INVALID_ARG (sizes, scale, max_q_len above
- * max_pages_per_seq * page_size, misaligned arrays), PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ * max_pages_per_seq * page_size, misaligned arrays, an unknown PA_PREFILL_PATH, a
+ * forced split-key launch needing more than 65535 query tiles of 32), PA_ERR_UNSUPPORTED,
+ * PA_ERR_HIP.
  */
 int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
                const int32_t* block_table, const int32_t* seq_lens, int causal,

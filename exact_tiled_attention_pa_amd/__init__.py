@@ -4,7 +4,8 @@ The compute path is the HIP library libpagedattn.so (C ABI in include/pagedattn.
 `binding` wraps it with ctypes.  `workloads` draws seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
-    EXPORTED, ContractError, KVLayout, PagedAttnError, PreparedPrefill, contract_violations,
+    EXPORTED, ContractError, KVLayout, PagedAttnError, PreparedDecode, PreparedPrefill,
+    contract_violations,
     decode_workspace,
     last_error, layout_of, set_contract_check,
     load_library, make_layout, pa_decode, pa_decode_combine, pa_decode_partial,

@@ -379,6 +379,35 @@ def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace, s
     return out
 
 
+class PreparedDecode:
+    """A pa_decode call (with its workspace) validated and marshalled once, then launched
+    any number of times on the same buffers: each launch is one C call.  With the
+    contract check on, it runs when the call is prepared.  Keeps its tensors alive."""
+
+    def __init__(self, q, k_pool, v_pool, block_table, seq_lens, scale, out, workspace,
+                 window: int = 0):
+        _decode_checks(q, k_pool, v_pool, block_table, seq_lens, workspace, out)
+        self._lay = layout_of(k_pool, block_table)
+        nbytes = workspace.numel() * workspace.element_size()
+        lib = load_library()
+        head = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                float(scale), _ptr(out), q.shape[0], q.shape[1])
+        tail = (_ptr(workspace), nbytes, ctypes.byref(self._lay))
+        if window:
+            self._fn, self._args = lib.pa_decode_window, head + (int(window),) + tail
+        else:
+            self._fn, self._args = lib.pa_decode, head + tail
+        self._tensors = (q, k_pool, v_pool, block_table, seq_lens, out, workspace)
+        self.out = out
+
+    def launch(self, stream=None):
+        """Enqueues both decode passes on `stream` (default: torch's current stream)."""
+        st = self._fn(*self._args, _stream(stream))
+        if st != PA_OK:
+            raise PagedAttnError(st, last_error())
+        return self.out
+
+
 # size of the library's static decode workspace (PA_NOALLOC_SCRATCH_BYTES in pagedattn.h)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 

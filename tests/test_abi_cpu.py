@@ -199,6 +199,8 @@ def test_binding_refuses_cpu_tensors():
         B.pa_prefill(q, q, q, q, q, True, 0.1, q, q, 4)
     with pytest.raises(ValueError):  # a prepared call runs the same checks, once
         B.PreparedPrefill(q, q, q, q, q, True, 0.1, q, q, 4)
+    with pytest.raises(ValueError):
+        B.PreparedDecode(q, q, q, q, q, 0.1, q, q)
 
 
 def test_kv_append_rejects(lib):

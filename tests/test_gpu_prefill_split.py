@@ -1,6 +1,7 @@
 """The split-key prefill kernel (32 query rows per workgroup, the key tiles dealt over
 its four waves, the waves' softmax states merged at the end) against the fp64 oracle,
-and the automatic choice between it and the 128-row tiled kernel.
+the automatic choice between it and the 128-row tiled kernel, and the binding's
+prepared calls (PreparedPrefill, PreparedDecode) against the direct ones.
 
 The shared small-shape parity tests already run under both kernels (the
 `prefill_path` fixture); these cases add what only the split kernel has: a key loop
@@ -127,3 +128,28 @@ def test_prepared_prefill_matches_direct_calls(window):
         torch.cuda.synchronize()
         assert torch.equal(got, ref), rnd
     G.compare(G.bf16_out_to_f64(ref), G.oracle_for(wl, call, window=window), "prepared")
+
+
+@pytest.mark.parametrize("window,hq", [(0, 4), (0, 16), (300, 4)])
+def test_prepared_decode_matches_direct_calls(window, hq):
+    """A PreparedDecode launched twice (new query values between the launches) returns
+    exactly what pa_decode returns, for both decode kernels and with a window."""
+    G.banner(f"prepared decode window={window} Hq={hq}")
+    wl = W.build("prepd", 92, heads=4, head_dim=128, page_size=16, lens=[1, 700, 3000],
+                 kind="decode", pool_slack=1.2, device="cuda", poison=True, q_heads=hq)
+    call = wl.calls[0]
+    out = torch.empty_like(call.q)
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    prep = B.PreparedDecode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens,
+                            wl.scale, out, ws, window=window)
+    ref = torch.empty_like(call.q)
+    ws2 = torch.empty_like(ws)
+    for rnd in range(2):
+        if rnd:
+            call.q.mul_(-0.5)
+        got = prep.launch().clone()
+        B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale,
+                    ref, ws2, window=window)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), rnd
+    G.compare(G.bf16_out_to_f64(ref), G.oracle_for(wl, call, window=window), "prepared decode")

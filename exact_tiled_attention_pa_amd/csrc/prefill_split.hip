@@ -164,9 +164,16 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   auto k_stage = [&](int s) { return my_lds + s * 2 * G::kTileBytes; };
   auto v_stage = [&](int s) { return my_lds + s * 2 * G::kTileBytes + G::kTileBytes; };
 
-  // Streams key tile j (64 keys from position 64j) of K and V into stage s of this wave:
-  // each 16-row group is one page's consecutive rows, one table entry, a buffer resource
-  // sized to its rows below seq_len.
+  // Physical pages of a tile's four 16-key groups, fetched one tile of this wave ahead of
+  // the loads that use them, so that each issue does not wait for its scalar loads.
+  int tbl[BN / 16];
+  auto fetch_table = [&](int j) {
+#pragma unroll
+    for (int g = 0; g < BN / 16; ++g) tbl[g] = bt[min((j * BN + 16 * g) >> log2_ps, last_page)];
+  };
+  // Streams key tile j (64 keys from position 64j; its pages in tbl) of K and V into
+  // stage s of this wave: each 16-row group is one page's consecutive rows, one table
+  // entry, a buffer resource sized to its rows below seq_len.
   auto issue_tile = [&](int j, int s) {
     const int kt0 = j * BN;
     char* const kd = k_stage(s);
@@ -174,7 +181,7 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int g = 0; g < BN / 16; ++g) {
       const int t0 = kt0 + 16 * g;
-      const int phys = bt[min(t0 >> log2_ps, last_page)];
+      const int phys = tbl[g];
       const int valid = min(16, seq_len - t0);
       const int bytes = valid > 0 ? valid * row_bytes_g : 0;
       const size_t elem =
@@ -312,18 +319,24 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int count = j0 < n_tiles ? (n_tiles - j0 + kWaves - 1) / kWaves : 0;
   constexpr int kLoadsPerTile = 2 * G::kInstPerTile;
   static_assert(kLoadsPerTile <= 63, "a tile's loads fit the load counter");
-  if (count > 0) issue_tile(j0, 0);
+  if (count > 0) {
+    fetch_table(j0);
+    issue_tile(j0, 0);
+    if (count > 1) fetch_table(j0 + kWaves);
+  }
   for (int it = 0; it < count; ++it) {
     const int j = j0 + it * kWaves;
     const int s = it % G::kStages;
     const bool more = it + 1 < count;
     if constexpr (G::kStages == 2) {
       // the other stage was last read by the previous tile; its reads have returned
-      // (their values fed that tile's MFMAs), and the wait makes that explicit
+      // (their values fed that tile's MFMAs), and the wait makes that explicit (it also
+      // covers the table entries fetched a tile ago)
       if (more) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __asm__ __volatile__("" ::: "memory");
         issue_tile(j + kWaves, 1 - s);
+        if (it + 2 < count) fetch_table(j + 2 * kWaves);
       }
       if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -338,6 +351,7 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __asm__ __volatile__("" ::: "memory");
         issue_tile(j + kWaves, 0);
+        if (it + 2 < count) fetch_table(j + 2 * kWaves);
       }
     }
     finish_tile(j);

@@ -87,6 +87,14 @@ def prefill_work(wl, call):
     return flops, nbytes
 
 
+def naive_attention_bytes(n: int, d: int, heads: int = 1) -> int:
+    """HBM bytes of the unfused three-step kernel for n x n attention in 16-bit floats,
+    8n^2 + 8nd per head: S and P each written and read once (8n^2), Q, K, V read and O
+    written once (8nd) ("What do FlashAttention and PagedAttention actually optimize?",
+    "Count the reads and writes FlashAttention removes")."""
+    return heads * (8 * n * n + 8 * n * d)
+
+
 def decode_kv_bytes(wl, call) -> int:
     """K and V bytes of every valid cached token (the decode metric)."""
     return int(call.seq_lens_host.astype("int64").sum()) * 2 * wl.heads * wl.head_dim * 2
@@ -358,6 +366,14 @@ def prefill_leg(wl, call, steps, warmup):
            "kernel_ms_min": roof["kernel_ms_min"],
            "us_per_call_wall": round(wall / steps * 1e6, 2), "flops_per_launch": flops,
            "alg_bytes_per_launch": nbytes, "roofline": roof}
+    n = int(call.seq_lens_host[0])
+    if call.batch == 1 and int(call.q_start_host[1]) == n:
+        # one square n x n attention per head: what the unfused kernel would move
+        naive = naive_attention_bytes(n, wl.head_dim, wl.num_q_heads)
+        res["naive_traffic"] = {
+            "bytes": naive, "formula": "heads * (8 N^2 + 8 N d)",
+            "measured_over_naive": (round(roof["traffic"] / naive, 4)
+                                    if roof.get("traffic") else None)}
     return res, out
 
 

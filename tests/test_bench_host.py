@@ -205,3 +205,24 @@ def test_rate_takes_the_average_from_the_whole_timed_region():
     assert r["frac"] == round(4000.0 / 2500.0, 4)
     assert r["kernel_ms_median"] == 2.35 and r["kernel_ms_min"] == 2.1
     assert r["kernel_ms_avg_paired"] == 2.45 and r["bound"] == "mfma"
+
+
+def test_naive_traffic_count_matches_the_pages_worked_figures():
+    """The unfused kernel's byte count the bench sets beside each prefill's measured
+    traffic reproduces the figures the page states for N = 4096, d = 128 (one head):
+    the S/P term about 134 MB, the Q/K/V/O term about 4 MB, S and P about 32 MiB each,
+    about 97 % of the traffic in S and P, and about 62 operations per byte against
+    4N^2 d + 3N^2 operations."""
+    import json
+    g = json.load(open(bench.os.path.join(bench.ROOT, "tests", "golden",
+                                          "naive_attention_traffic.json")))
+    n, d = g["N"], g["d"]
+    total = bench.naive_attention_bytes(n, d)
+    sp, nd = bench.naive_attention_bytes(n, 0), total - bench.naive_attention_bytes(n, 0)
+    assert round(sp / 1e6) == g["s_p_term_mb_about"]
+    assert round(nd / 1e6) == g["nd_term_mb_about"]
+    assert round(2 * n * n / 2 ** 20) == g["s_or_p_mib_about"]  # one 16-bit n x n matrix
+    assert round(sp / total, 2) == g["s_p_share_about"]
+    ops = 4 * n * n * d + 3 * n * n
+    assert round(ops / total) == g["ops_per_byte_about"]
+    assert bench.naive_attention_bytes(n, d, heads=32) == 32 * total

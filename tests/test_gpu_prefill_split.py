@@ -153,3 +153,23 @@ def test_prepared_decode_matches_direct_calls(window, hq):
         torch.cuda.synchronize()
         assert torch.equal(got, ref), rnd
     G.compare(G.bf16_out_to_f64(ref), G.oracle_for(wl, call, window=window), "prepared decode")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_split_and_tiled_kernels_agree_on_every_element_at_4096(causal, monkeypatch):
+    """The two prefill kernels over the N=4096, 32-head workload (the split-key one forced:
+    4096 workgroups), compared on every output element, plus sampled rows of each against
+    the oracle.  Two independent decompositions of the same exact result."""
+    G.banner(f"split vs tiled prefill, N=4096 causal={causal}")
+    wl = W.prefill_4096(causal=causal, device="cuda")
+    call = wl.calls[0]
+    outs = {}
+    for path in ("tiles", "split"):
+        monkeypatch.setenv("PA_PREFILL_PATH", path)
+        outs[path] = _prefill(wl, call)
+    G.compare(G.bf16_out_to_f64(outs["split"]), G.bf16_out_to_f64(outs["tiles"]),
+              "split vs tiled", max_tol=8e-3, mean_tol=5e-4)
+    rows = {0: G.spread_rows(4096, 128, seed=11)}
+    ref = G.oracle_for(wl, call, rows=rows)
+    for path, out in outs.items():
+        G.compare(G.bf16_out_to_f64(out), ref, f"N=4096 {path}")

@@ -101,6 +101,39 @@ def test_random_prefill(seed, prefill_path):
     G.compare(G.bf16_out_to_f64(out), ref, f"random prefill seed={seed}")
 
 
+def short_chunk_case(seed):
+    """Chunks of a few rows on caches of up to 6,000 keys: the split-key prefill's
+    regime (each wave of a 32-row workgroup walks a quarter of a long key range)."""
+    rng = np.random.default_rng(5000 + seed)
+    d = int(rng.choice([64, 128]))
+    ps = int(rng.choice([16, 32, 64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4]))
+    batch = int(rng.integers(1, 4))
+    lens = _lens(rng, batch, 6000)
+    q_lens = [int(rng.choice([min(L, x) for x in (1, 2, 7, 31, 32, 33, 64)])) for L in lens]
+    causal = bool(rng.random() < 0.75)
+    window = int(rng.choice([0, 0, 1, 40, 700, 5000])) if causal else 0
+    return d, ps, hkv, hkv * g, lens, q_lens, causal, window
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_short_chunks(seed, prefill_path):
+    d, ps, hkv, hq, lens, q_lens, causal, window = short_chunk_case(seed)
+    G.banner(f"random short chunks seed={seed} d={d} ps={ps} Hkv={hkv} Hq={hq} lens={lens} "
+             f"q_lens={q_lens} causal={causal} window={window}")
+    wl = W.build("rshort", 6000 + seed, heads=hkv, head_dim=d, page_size=ps, lens=lens,
+                 q_lens=q_lens, causal=causal, pool_slack=1.2, device="cuda", poison=True,
+                 q_heads=hq)
+    call = wl.calls[0]
+    out = torch.full_like(call.q, float("nan"))
+    B.pa_prefill(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, causal,
+                 wl.scale, out, call.q_start, call.max_q_len, window=window)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, window=window),
+              f"random short chunks seed={seed}")
+
+
 def test_many_short_sequences_decode_and_prefill(prefill_path):
     """Thousands of short decode sequences (grid z in the thousands, one chunk per
     split) and hundreds of short prefill chunks in one call."""

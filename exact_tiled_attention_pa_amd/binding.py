@@ -143,7 +143,10 @@ _lib = None
 
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     """Loads libpagedattn.so (built in-tree by __graft_entry__.build or
-    `python -m exact_tiled_attention_pa_amd.build`).  Raises if it is missing."""
+    `python -m exact_tiled_attention_pa_amd.build`) and returns its handle; raises if it
+    is missing.  Without `path` the in-tree library is loaded once and is the one every
+    call of this module uses; with `path` that file is loaded and its handle returned,
+    and the module's calls keep using their own library."""
     global _lib
     if _lib is not None and path is None:
         return _lib

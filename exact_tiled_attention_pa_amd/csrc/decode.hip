@@ -31,8 +31,9 @@
 //     m, running sum l, output accumulator; "Flash Attention: Fast, Memory-Efficient
 //     Attention for LLMs", "The Algorithm"); the waves' states are merged through LDS
 //     and the unit's (m, l, unnormalised O) goes to the workspace.
-//   pass 2 (decode_combine_kernel): one wave per (sequence, head) merges the
-//     splits' partials in order with the same rescaling algebra and writes bf16 O.
+//   pass 2 (decode_combine_kernel): four waves per (sequence, head) each merge every
+//     fourth split's partial in order with the same rescaling algebra; their states
+//     merge through LDS and one wave writes bf16 O.
 //
 // Query head h reads K/V head h / (num_q_heads / num_kv_heads).  m is kept in
 // log2 units (scores times scale * log2(e)) so every exponential is one v_exp_f32.
@@ -431,11 +432,14 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// One wave per (sequence, head), four heads per workgroup: the wave walks the splits
-// in order with the same online rescaling as pass 1 (running max, rescaled sum and
-// output), each lane holding D / 64 output columns, and writes O / l as bf16.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineHeads = kCombineThreads / 64;
+// Four waves per (sequence, head): wave w folds splits w, w + 4, w + 8, ... in order with
+// the same online rescaling as pass 1 (running max, rescaled sum and output), each lane
+// holding D / 64 output columns; the four states then merge through LDS with the same
+// algebra (weights 2^(m_w - M)) and wave 0 writes O / l as bf16.  Four chains of a
+// quarter of the splits each: the fold is a chain of dependent steps, and a long
+// sequence's 128 or more splits in one chain made the pass latency-bound.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineThreads = 64 * kCombineWaves;
 
 template <int D>
 __global__ void __launch_bounds__(kCombineThreads)
@@ -444,9 +448,11 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
                       int num_q_heads, int split_tokens, int max_splits, int window,
                       int window_aligned) {
   constexpr int kPerLane = D / 64;
+  __shared__ float st_ml[kCombineWaves][2];
+  __shared__ float st_o[kCombineWaves][D];
   const int lane = threadIdx.x & 63;
-  const int h = blockIdx.x * kCombineHeads + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (h >= num_q_heads) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int seq_len = seq_lens[b];
   // splits holding keys: with a window, the window-aligned splits of the
@@ -462,15 +468,16 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
   float acc[kPerLane];
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e) acc[e] = 0.f;
-  // splits in groups of kGroup: every load of a group is issued before any of its
-  // partials is folded in (absent splits of the last group fold in with weight 0)
+  // this wave's splits in groups of kGroup: every load of a group is issued before any
+  // of its partials is folded in (absent splits of the last group fold in with weight 0)
   constexpr int kGroup = 8;
-  for (int s0 = s_first; s0 < n_splits; s0 += kGroup) {
+  for (int s0 = s_first + wave; s0 < n_splits; s0 += kCombineWaves * kGroup) {
     float ms[kGroup], ls[kGroup], os[kGroup][kPerLane];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
-      const int s = min(s0 + i, n_splits - 1);
-      ms[i] = s0 + i < n_splits ? ws_ml[(slot0 + s) * 2] : kEmptyMax;
+      const int si = s0 + kCombineWaves * i;
+      const int s = min(si, n_splits - 1);
+      ms[i] = si < n_splits ? ws_ml[(slot0 + s) * 2] : kEmptyMax;
       ls[i] = ws_ml[(slot0 + s) * 2 + 1];
 #pragma unroll
       for (int e = 0; e < kPerLane; ++e) os[i][e] = ws_o[(slot0 + s) * D + lane * kPerLane + e];
@@ -486,10 +493,33 @@ decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restr
       m = m_new;
     }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  // merge: a wave with no split holds m = kEmptyMax, l = 0, O = 0 and gets weight 0
+  if (lane == 0) {
+    st_ml[wave][0] = m;
+    st_ml[wave][1] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) st_o[wave][lane * kPerLane + e] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float big = st_ml[0][0];
+#pragma unroll
+  for (int w = 1; w < kCombineWaves; ++w) big = fmaxf(big, st_ml[w][0]);
+  float lt = 0.f;
+  float ot[kPerLane];
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) ot[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) {
+    const float a = fast_exp2(st_ml[w][0] - big);
+    lt = fmaf(a, st_ml[w][1], lt);
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) ot[e] = fmaf(a, st_o[w][lane * kPerLane + e], ot[e]);
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   uint16_t* dst = out + ((size_t)b * num_q_heads + h) * D + lane * kPerLane;
 #pragma unroll
-  for (int e = 0; e < kPerLane; ++e) dst[e] = to_bf16_bits(acc[e] * inv);
+  for (int e = 0; e < kPerLane; ++e) dst[e] = to_bf16_bits(ot[e] * inv);
 }
 
 // Compute units of the current device, looked up once per device (pass 1 runs one
@@ -531,7 +561,7 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((a.num_q_heads + kCombineHeads - 1) / kCombineHeads, a.batch);
+  const dim3 grid(a.num_q_heads, a.batch);
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(kCombineThreads), 0, stream,
                        a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,

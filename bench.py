@@ -195,8 +195,16 @@ def prefill_kernel_name(wl, call) -> str:
     return f"prefill_kernel<{wl.head_dim}, {causal}, {str(wl.page_size >= 64).lower()}>"
 
 
-def decode_kernel_name(wl) -> str:
-    return f"{KERNEL_FILES[decode_kind(wl)]}<{wl.head_dim}>"
+def decode_kernel_name(wl, call) -> str:
+    """The pass-1 instantiation a decode call runs: the grouped-head kernel, or the
+    one-head-per-row kernel with the split length the library picks for this batch
+    (in steps of 32 keys)."""
+    if decode_kind(wl) == "decode_gqa":
+        return f"decode_gqa_kernel<{wl.head_dim}>"
+    from exact_tiled_attention_pa_amd import binding as B
+    split = B.pa_decode_split_tokens(call.batch, wl.num_q_heads,
+                                     B.layout_of(wl.k_pool, call.block_table))
+    return f"decode_partial_kernel<{wl.head_dim}, {split // 32}>"
 
 
 def timing_stats(ms):
@@ -327,7 +335,7 @@ def decode_leg(wl, call, steps, warmup):
     wall, split_t, comb_t = timed_decode(wl, call, out, steps, warmup)
     ms_step = wall / steps * 1e3
     roof = _rate(nbytes, split_t, HBM_PEAK_GBS, "GB/s", bound="hbm",
-                 kernel=decode_kernel_name(wl))
+                 kernel=decode_kernel_name(wl, call))
     cst = timing_stats(comb_t.pairs)
     roof.update(traffic=recorded_traffic(decode_kind(wl), wl.name),
                 combine_ms_avg=round(comb_t.avg, 4), combine_ms_median=_ms(cst, "median"))
@@ -425,7 +433,7 @@ def next_rows_summary(decode_wl, steps, warmup):
                                                        gc.block_table, gc.seq_lens, g.scale,
                                                        ws), steps, warmup)
     res["gqa_decode"] = _rate(decode_kv_bytes(g, gc), tm, HBM_PEAK_GBS, "GB/s", bound="hbm",
-                              workload=g.name, kernel=decode_kernel_name(g),
+                              workload=g.name, kernel=decode_kernel_name(g, gc),
                               traffic=recorded_traffic("decode_gqa", g.name))
     del g, gc, ws
 

@@ -162,7 +162,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_prefill.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, lay]
     lib.pa_decode_workspace_bytes.restype = sz
-    lib.pa_decode_split_tokens.argtypes = [i32, lay]
+    lib.pa_decode_split_tokens.argtypes = [i32, i32, lay]
     lib.pa_decode_split_tokens.restype = i32
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, f32, vp, i32, i32, vp, sz, lay, vp]
     lib.pa_decode.restype = ctypes.c_int
@@ -331,8 +331,9 @@ def pa_decode_workspace_bytes(batch: int, num_q_heads: int, layout: KVLayout) ->
                                                         ctypes.byref(layout)))
 
 
-def pa_decode_split_tokens(num_q_heads: int, layout: KVLayout) -> int:
-    return int(load_library().pa_decode_split_tokens(int(num_q_heads), ctypes.byref(layout)))
+def pa_decode_split_tokens(batch: int, num_q_heads: int, layout: KVLayout) -> int:
+    return int(load_library().pa_decode_split_tokens(int(batch), int(num_q_heads),
+                                                     ctypes.byref(layout)))
 
 
 def decode_workspace(q, k_pool, block_table) -> torch.Tensor:

@@ -84,37 +84,52 @@ int check_scale(float scale) {
   return PA_OK;
 }
 
-// Keys per decode split: grouped heads walk longer splits (their workgroups read a
+// Units of pass-1 work below which the one-head-per-row decode shortens its splits: the
+// MI355X's 256 CUs each run one persistent workgroup that claims units.
+constexpr int64_t kDecodeFillUnits = 256;
+
+// Keys per decode split.  Grouped heads walk longer splits (their workgroups read a
 // quarter of the bytes per key that one-head-per-row workgroups do, so a longer split
-// keeps the per-workgroup set-up and merge small against the streaming).
-int split_tokens_of(const pa_kv_layout* layout, int32_t num_q_heads) {
+// keeps the per-workgroup set-up and merge small against the streaming).  The
+// one-head-per-row decode takes 256-key splits, halved (to 128, then 64) while a batch
+// of this many sequences, each as long as the table allows, would give pass 1 fewer
+// units (split x group of the heads one wave load covers) than there are CUs: a small
+// batch then still spreads over the chip instead of leaving CUs idle.
+int split_tokens_of(const pa_kv_layout* layout, int32_t num_q_heads, int32_t batch) {
   if (num_q_heads / layout->num_kv_heads >= pa::kGqaMinGroup)
     return pa::kDecodeSplitTokensGrouped;
-  return layout->page_size > pa::kDecodeSplitTokens ? layout->page_size
-                                                     : pa::kDecodeSplitTokens;
+  const int64_t tokens = (int64_t)layout->max_pages_per_seq * layout->page_size;
+  const int heads_per_load = 64 / (layout->head_dim / 8);  // 4 at d = 128, 8 at d = 64
+  const int64_t groups = (num_q_heads + heads_per_load - 1) / heads_per_load;
+  int st = pa::kDecodeSplitTokens;
+  while (st > pa::kDecodeSplitTokens / 4 &&
+         (int64_t)batch * ((tokens + st - 1) / st) * groups < kDecodeFillUnits)
+    st /= 2;
+  return st;
 }
 
-int max_splits_of(const pa_kv_layout* layout, int32_t num_q_heads) {
+int max_splits_of(const pa_kv_layout* layout, int32_t num_q_heads, int32_t batch) {
   const int64_t tokens = (int64_t)layout->max_pages_per_seq * layout->page_size;
-  const int st = split_tokens_of(layout, num_q_heads);
+  const int st = split_tokens_of(layout, num_q_heads, batch);
   return (int)((tokens + st - 1) / st);
 }
 
 // Workspace: fp32 O partials first, then (m, l) pairs, each region 256-byte aligned.
 size_t ws_o_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
-  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout, num_q_heads) * layout->head_dim;
+  const size_t n =
+      (size_t)batch * num_q_heads * max_splits_of(layout, num_q_heads, batch) * layout->head_dim;
   return (n * sizeof(float) + 255) / 256 * 256;
 }
 
 size_t ws_ml_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
-  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout, num_q_heads) * 2;
+  const size_t n = (size_t)batch * num_q_heads * max_splits_of(layout, num_q_heads, batch) * 2;
   return (n * sizeof(float) + 255) / 256 * 256;
 }
 
 // Pass 1's plan of the one-head-per-row decode: a claim counter, the number of
 // (sequence, split) pairs and the pairs themselves.
 size_t ws_plan_bytes(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
-  const size_t n = 2 + (size_t)batch * max_splits_of(layout, num_q_heads);
+  const size_t n = 2 + (size_t)batch * max_splits_of(layout, num_q_heads, batch);
   return (n * sizeof(int32_t) + 255) / 256 * 256;
 }
 
@@ -143,13 +158,15 @@ int check_decode_common(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* 
     if (st) return st;
   }
   if (!seq_lens) return fail(PA_ERR_NULL, "seq_lens must be non-NULL");
-  if (max_splits_of(layout, num_q_heads) > 65535)
+  if (max_splits_of(layout, num_q_heads, batch) > 65535)
     return fail(PA_ERR_INVALID_ARG, "max_pages_per_seq * page_size = %lld needs more than 65535 "
                 "decode splits", (long long)layout->max_pages_per_seq * layout->page_size);
   // pass 1 numbers its units of work (split x head group) with 32-bit integers
-  if ((int64_t)batch * max_splits_of(layout, num_q_heads) * num_q_heads >= ((int64_t)1 << 31))
+  if ((int64_t)batch * max_splits_of(layout, num_q_heads, batch) * num_q_heads >=
+      ((int64_t)1 << 31))
     return fail(PA_ERR_INVALID_ARG, "%d sequences x %d splits x %d query heads exceed 2^31 "
-                "decode work units", batch, max_splits_of(layout, num_q_heads), num_q_heads);
+                "decode work units", batch, max_splits_of(layout, num_q_heads, batch),
+                num_q_heads);
   if (!check_workspace) return PA_OK;
   const size_t need = ws_bytes(batch, num_q_heads, layout);
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
@@ -185,8 +202,8 @@ pa::DecodeArgs decode_args(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf1
   a.head_dim = layout->head_dim;
   a.log2_page_size = log2_exact(layout->page_size);
   a.max_pages_per_seq = layout->max_pages_per_seq;
-  a.split_tokens = split_tokens_of(layout, num_q_heads);
-  a.max_splits = max_splits_of(layout, num_q_heads);
+  a.split_tokens = split_tokens_of(layout, num_q_heads, batch);
+  a.max_splits = max_splits_of(layout, num_q_heads, batch);
   a.window = window;
   return a;
 }
@@ -286,9 +303,9 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
   return ws_bytes(batch, num_q_heads, layout);
 }
 
-int32_t pa_decode_split_tokens(int32_t num_q_heads, const pa_kv_layout* layout) {
-  if (check_layout(layout, num_q_heads) != PA_OK) return 0;
-  return split_tokens_of(layout, num_q_heads);
+int32_t pa_decode_split_tokens(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout) {
+  if (check_layout(layout, num_q_heads) != PA_OK || batch < 0) return 0;
+  return split_tokens_of(layout, num_q_heads, batch);
 }
 
 int pa_decode_partial(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,

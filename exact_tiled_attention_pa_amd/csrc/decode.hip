@@ -8,9 +8,10 @@
 // way HBM likes them:
 //
 //   pass 1 (decode_plan_kernel, then decode_partial_kernel): the work is a list of
-//     (sequence, split) pairs, a split being 256 consecutive keys (with a sliding
-//     window the splits are laid back from the sequence end, so a window of w keys
-//     takes ceil(w / 256) of them), times the head groups: a head group is the heads
+//     (sequence, split) pairs, a split being S = 256 consecutive keys, or 128 or 64
+//     for batches too small to give every CU a unit with 256 (with a sliding window the
+//     splits are laid back from the sequence end, so a window of w keys takes
+//     ceil(w / S) of them), times the head groups: a head group is the heads
 //     one wave load covers, 64 lanes x 16 B = 1 KB = one token's row for 4 adjacent
 //     heads at d = 128 (8 at d = 64), contiguous in the pool's [page, slot, head, d]
 //     layout.  A one-workgroup plan pass lists the pairs and zeroes a claim counter in
@@ -55,11 +56,16 @@ constexpr int kRing = 2;                     // register slots per streaming wav
 constexpr int kAhead = kRing - 1;            // steps in flight ahead of the one consumed
 constexpr int kQueue = 4;                    // split descriptors held in LDS
 constexpr int kItemPages = 32;               // pages one split may touch (<= 17 here)
-constexpr int kSplitTokensMha = kDecodeSplitTokens;  // keys per split
-constexpr int kSplitSteps = kSplitTokensMha / kChunk;  // 8 steps of 32 keys
-constexpr int kMidStep = 4;                  // step at which the next split is published
-static_assert(kSplitSteps % kRing == 0, "every split starts in ring slot 0");
-static_assert(kSplitSteps - kAhead >= kMidStep, "the next split is known before its loads");
+// A split is STEPS steps of kChunk keys: 8 (256 keys), or 4 and 2 (128 and 64 keys) for
+// batches too small to give every CU a unit of work with 256-key splits.
+template <int STEPS>
+struct SplitShape {
+  static constexpr int kSteps = STEPS;
+  static constexpr int kTokens = STEPS * kChunk;
+  static constexpr int kMidStep = STEPS / 2;  // step at which the next split is published
+  static_assert(kSteps % kRing == 0, "every split starts in ring slot 0");
+  static_assert(kSteps - kAhead >= kMidStep, "the next split is known before its loads");
+};
 constexpr float kEmptyMax = -1e30f;          // running max before any visible key (finite)
 constexpr int kPlanThreads = 1024;
 
@@ -98,20 +104,21 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// Split key range [t_begin, t_end) of split `split` of a sequence of seq_len keys.
-// Without a window split s covers keys 256 s .. 256 s + 255; with a sliding window the
-// splits are laid back from the sequence end, so a window of w keys takes
-// ceil(min(w, L) / 256) splits of at most 256 keys, the first one reaching back to the
+// Split key range [t_begin, t_end) of split `split` of a sequence of seq_len keys, splits
+// of S keys.  Without a window split s covers keys S s .. S s + S - 1; with a sliding
+// window the splits are laid back from the sequence end, so a window of w keys takes
+// ceil(min(w, L) / S) splits of at most S keys, the first one reaching back to the
 // window's first key (keys before it are masked).
+template <int S>
 __device__ __forceinline__ void split_range(int seq_len, int split, int window, int& t_begin,
                                             int& t_end) {
   if (window > 0) {
-    const int n = window_split_count(seq_len, window, kSplitTokensMha);
-    t_end = seq_len - (n - 1 - split) * kSplitTokensMha;
-    t_begin = max(0, t_end - kSplitTokensMha);
+    const int n = window_split_count(seq_len, window, S);
+    t_end = seq_len - (n - 1 - split) * S;
+    t_begin = max(0, t_end - S);
   } else {
-    t_begin = split * kSplitTokensMha;
-    t_end = min(seq_len, t_begin + kSplitTokensMha);
+    t_begin = split * S;
+    t_end = min(seq_len, t_begin + S);
   }
 }
 
@@ -141,10 +148,23 @@ decode_plan_kernel(const int32_t* __restrict__ seq_lens, int batch, int split_to
       scan[threadIdx.x] += add;
       __syncthreads();
     }
-    const int first = base + scan[threadIdx.x] - n;
-    // packed unsigned: sequence indices reach 65534, past the int32 sign bit once shifted
-    for (int i = 0; i < n; ++i) plan[2 + first + i] = (int32_t)(((uint32_t)b << 16) | (uint32_t)i);
-    base += scan[kPlanThreads - 1];
+    // the chunk's pairs, written by all threads in order: entry e belongs to the first
+    // sequence t of the chunk whose inclusive count exceeds e (a binary search of the
+    // scan), as its split e - (count before t); one thread per sequence writing its own
+    // pairs would serialise a long sequence's hundreds of splits
+    const int total = scan[kPlanThreads - 1];
+    for (int e = (int)threadIdx.x; e < total; e += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] > e) hi = mid;
+        else lo = mid + 1;
+      }
+      const int split = e - (lo > 0 ? scan[lo - 1] : 0);
+      // packed unsigned: sequence indices reach 65534, past the int32 sign bit once shifted
+      plan[2 + base + e] = (int32_t)(((uint32_t)(c + lo) << 16) | (uint32_t)split);
+    }
+    base += total;
     __syncthreads();
   }
   if (threadIdx.x == 0) {
@@ -159,7 +179,7 @@ decode_plan_kernel(const int32_t* __restrict__ seq_lens, int batch, int split_to
 // split the streaming waves finished last; it issues every vector memory operation
 // besides the K/V stream, so the streaming waves' wait counts cover their own loads
 // only and their stream runs on across split boundaries without draining.
-template <int D>
+template <int D, int STEPS>
 __global__ void __launch_bounds__(kThreads)
 decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
                       const uint16_t* __restrict__ v_pool,
@@ -169,6 +189,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       float scale_log2, int num_q_heads, int num_kv_heads, int log2_ps,
                       int max_pages, int max_splits, int window) {
   using G = DecodeGeometry<D>;
+  using SS = SplitShape<STEPS>;
   constexpr uint32_t kOutside = 0x80000000u;   // a load offset past every buffer
   constexpr uint32_t kAllBytes = 0x7fffffffu;  // buffer size: offsets are checked here
   __shared__ __attribute__((aligned(1024))) DecodeShared<D> sh;
@@ -196,7 +217,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       c = Claim{1, (int)(pair >> 16), (int)(pair & 0xffffu), qi % n_hg};
       const int seq_len = seq_lens[c.b];
       int t_begin, t_end;
-      split_range(seq_len, c.split, window, t_begin, t_end);
+      split_range<SS::kTokens>(seq_len, c.split, window, t_begin, t_end);
       const int page0 = t_begin >> log2_ps;
       if (lane <= ((t_end - 1) >> log2_ps) - page0)
         d.pages[lane] = block_table[(size_t)c.b * max_pages + page0 + lane];
@@ -292,7 +313,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   };
 
   // K/V rows of the steps in flight, in registers: step si of a split sits in slot
-  // si % kRing (a split is kSplitSteps steps, a multiple of kRing, so each starts in
+  // si % kRing (a split is SS::kSteps steps, a multiple of kRing, so each starts in
   // slot 0), token i of
   // the wave's 4 at [slot][i]
   u32x4 kr[kRing][kStep], vr[kRing][kStep];
@@ -383,8 +404,8 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   for (int k = 0;; ++k) {
 #pragma unroll
-    for (int si = 0; si < kSplitSteps; ++si) {
-      if (si == kMidStep) {
+    for (int si = 0; si < SS::kSteps; ++si) {
+      if (si == SS::kMidStep) {
         lds_barrier();  // split k + 1 published
         int n_hg;
         load_desc(sh.desc[(k + 1) % kQueue], n_valid, n_tb, n_te, n_tlo, n_page0, n_pages, n_hg);
@@ -393,11 +414,11 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // step si + kAhead of this split, or one of the next split's first steps, into the
       // slot the previous step was consumed from
       const int ahead = si + kAhead;
-      if (ahead < kSplitSteps)
+      if (ahead < SS::kSteps)
         issue(c_valid, c_tb, c_te, c_tlo, c_page0, c_pages, lane_off, ahead,
               kr[ahead % kRing], vr[ahead % kRing]);
       else
-        issue(n_valid, n_tb, n_te, n_tlo, n_page0, n_pages, n_lane_off, ahead - kSplitSteps,
+        issue(n_valid, n_tb, n_te, n_tlo, n_page0, n_pages, n_lane_off, ahead - SS::kSteps,
               kr[ahead % kRing], vr[ahead % kRing]);
       consume(si, kr[si % kRing], vr[si % kRing]);
       // keep the steps in program order: hoisting later steps' loads and address work
@@ -432,22 +453,21 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// Four waves per (sequence, head): wave w folds splits w, w + 4, w + 8, ... in order with
+// WAVES waves per (sequence, head): wave w folds splits w, w + WAVES, ... in order with
 // the same online rescaling as pass 1 (running max, rescaled sum and output), each lane
-// holding D / 64 output columns; the four states then merge through LDS with the same
-// algebra (weights 2^(m_w - M)) and wave 0 writes O / l as bf16.  Four chains of a
-// quarter of the splits each: the fold is a chain of dependent steps, and a long
-// sequence's 128 or more splits in one chain made the pass latency-bound.
-constexpr int kCombineWaves = 4;
-constexpr int kCombineThreads = 64 * kCombineWaves;
-
-template <int D>
-__global__ void __launch_bounds__(kCombineThreads)
+// holding D / 64 output columns; the states then merge through LDS with the same
+// algebra (weights 2^(m_w - M)) and wave 0 writes O / l as bf16.  The fold is a chain of
+// dependent steps, so a long sequence's splits in one chain made the pass
+// latency-bound: 4 waves, or 16 when the launch has fewer (sequence, head) pairs than
+// the chip has CUs (a small batch, whose splits are short and many).
+template <int D, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
 decode_combine_kernel(const int32_t* __restrict__ seq_lens, const float* __restrict__ ws_o,
                       const float* __restrict__ ws_ml, uint16_t* __restrict__ out,
                       int num_q_heads, int split_tokens, int max_splits, int window,
                       int window_aligned) {
   constexpr int kPerLane = D / 64;
+  constexpr int kCombineWaves = WAVES;
   __shared__ float st_ml[kCombineWaves][2];
   __shared__ float st_o[kCombineWaves][D];
   const int lane = threadIdx.x & 63;
@@ -539,11 +559,12 @@ int cu_count() {
   return n;
 }
 
-template <int D>
+template <int D, int STEPS>
 void launch_partial(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
                      a.batch, a.split_tokens, a.max_splits, a.window, a.plan);
-  hipLaunchKernelGGL(decode_partial_kernel<D>, dim3(cu_count()), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((decode_partial_kernel<D, STEPS>), dim3(cu_count()), dim3(kThreads), 0,
+                     stream,
                      a.q, a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
                      a.plan, score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
                      a.log2_page_size, a.max_pages_per_seq, a.max_splits, a.window);
@@ -553,24 +574,29 @@ void launch_partial(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   if (decode_grouped(a)) return launch_decode_partial_gqa(a, stream);
-  // one-head-per-row splits are kSplitTokensMha keys (pages hold at most 256 tokens)
-  if (a.split_tokens != kSplitTokensMha) return hipErrorInvalidValue;
-  if (a.head_dim == 128) launch_partial<128>(a, stream);
-  else launch_partial<64>(a, stream);
+  // one-head-per-row splits of 256, 128 or 64 keys (the host layer picks the length)
+  const bool d128 = a.head_dim == 128;
+  switch (a.split_tokens) {
+    case 8 * kChunk: d128 ? launch_partial<128, 8>(a, stream) : launch_partial<64, 8>(a, stream); break;
+    case 4 * kChunk: d128 ? launch_partial<128, 4>(a, stream) : launch_partial<64, 4>(a, stream); break;
+    case 2 * kChunk: d128 ? launch_partial<128, 2>(a, stream) : launch_partial<64, 2>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
+template <int D, int WAVES>
+void launch_combine(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.batch);
-  if (a.head_dim == 128) {
-    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(kCombineThreads), 0, stream,
-                       a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
-                       a.max_splits, a.window, decode_grouped(a) ? 0 : 1);
-  } else {
-    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(kCombineThreads), 0, stream,
-                       a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
-                       a.max_splits, a.window, decode_grouped(a) ? 0 : 1);
-  }
+  hipLaunchKernelGGL((decode_combine_kernel<D, WAVES>), grid, dim3(64 * WAVES), 0, stream,
+                     a.seq_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, a.split_tokens,
+                     a.max_splits, a.window, decode_grouped(a) ? 0 : 1);
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
+  const bool wide = (long long)a.num_q_heads * a.batch < cu_count();
+  if (a.head_dim == 128) wide ? launch_combine<128, 16>(a, stream) : launch_combine<128, 4>(a, stream);
+  else wide ? launch_combine<64, 16>(a, stream) : launch_combine<64, 4>(a, stream);
   return hipGetLastError();
 }
 

@@ -137,10 +137,13 @@ int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                  const pa_kv_layout* layout);
 
-/* Key positions covered by one decode split (a multiple of page_size): 256 (or
- * page_size, if larger) when each query head has its own K/V head, 1024 when
- * num_q_heads / num_kv_heads >= 4.  0 for an invalid layout or head count. */
-int32_t pa_decode_split_tokens(int32_t num_q_heads, const pa_kv_layout* layout);
+/* Key positions covered by one decode split of a batch of `batch` sequences: 1024 when
+ * num_q_heads / num_kv_heads >= 4; otherwise 256, halved to 128 and then 64 while
+ * batch * ceil(max_pages_per_seq * page_size / split) * ceil(num_q_heads / h) < 256
+ * (h = 4 heads at head_dim 128, 8 at 64: the heads one 1 KB wave load covers), so
+ * that a small batch still gives each of the chip's 256 CUs a unit of work.  0 for an
+ * invalid layout, head count or batch. */
+int32_t pa_decode_split_tokens(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout);
 
 /*
  * pa_decode -- one new query token per sequence attending over all L_b cached

@@ -97,8 +97,8 @@ def test_token_rows_above_32_mib_are_rejected(lib):
     assert "2^24" in B.last_error()
     # exactly 2^24 elements per token row is accepted
     ok = lay(hkv=131072, d=128)
-    assert lib.pa_decode_split_tokens(131072, ctypes.byref(ok)) == 256
-    assert lib.pa_decode_split_tokens(131073, ctypes.byref(layout)) == 0
+    assert lib.pa_decode_split_tokens(64, 131072, ctypes.byref(ok)) == 256
+    assert lib.pa_decode_split_tokens(64, 131073, ctypes.byref(layout)) == 0
 
 
 def test_prefill_empty_batch_is_ok_without_device(lib):
@@ -110,23 +110,23 @@ def test_prefill_empty_batch_is_ok_without_device(lib):
 def test_decode_workspace_size_formula(lib):
     layout = B.make_layout(17000, 16, 32, 128, 512)
     # 512 pages x 16 tokens, 256-token splits -> 32 splits per sequence
-    assert lib.pa_decode_split_tokens(32, ctypes.byref(layout)) == 256
+    assert lib.pa_decode_split_tokens(64, 32, ctypes.byref(layout)) == 256
     o = 64 * 32 * 32 * 128 * 4
     ml = 64 * 32 * 32 * 2 * 4
     r = lambda n: (n + 255) // 256 * 256
     plan = (2 + 64 * 32) * 4  # claim counter, pair count, (sequence, split) pairs
     assert lib.pa_decode_workspace_bytes(64, 32, ctypes.byref(layout)) == r(o) + r(ml) + r(plan)
     big = B.make_layout(128, 256, 8, 128, 128)
-    assert lib.pa_decode_split_tokens(8, ctypes.byref(big)) == 256
+    assert lib.pa_decode_split_tokens(64, 8, ctypes.byref(big)) == 256
     bad = B.make_layout(128, 24, 8, 128, 128)
     assert lib.pa_decode_workspace_bytes(1, 8, ctypes.byref(bad)) == 0
-    assert lib.pa_decode_split_tokens(8, ctypes.byref(bad)) == 0
+    assert lib.pa_decode_split_tokens(64, 8, ctypes.byref(bad)) == 0
     # grouped heads: 8 K/V heads, 2 query heads each keep 256-token splits; 4 or more
     # per K/V head walk 1024-token splits -> 8 splits of 8192 tokens
     gl = B.make_layout(17000, 16, 8, 128, 512)
-    assert lib.pa_decode_split_tokens(16, ctypes.byref(gl)) == 256
-    assert lib.pa_decode_split_tokens(64, ctypes.byref(gl)) == 1024
-    assert lib.pa_decode_split_tokens(12, ctypes.byref(gl)) == 0  # not a multiple of 8
+    assert lib.pa_decode_split_tokens(64, 16, ctypes.byref(gl)) == 256
+    assert lib.pa_decode_split_tokens(64, 64, ctypes.byref(gl)) == 1024
+    assert lib.pa_decode_split_tokens(64, 12, ctypes.byref(gl)) == 0  # not a multiple of 8
     o = 64 * 64 * 8 * 128 * 4
     ml = 64 * 64 * 8 * 2 * 4
     plan = (2 + 64 * 8) * 4
@@ -253,3 +253,26 @@ def test_prefill_path_override_is_checked(lib, monkeypatch):
     monkeypatch.setenv("PA_PREFILL_PATH", "split")
     assert prefill(lib, big, max_q_len=32 * 65535 + 1) == B.PA_ERR_INVALID_ARG
     assert "split-key" in B.last_error()
+
+
+def test_small_batches_take_shorter_decode_splits(lib):
+    """One-head-per-row decode: 256-key splits unless the batch would give pass 1 fewer
+    units (split x group of 4 heads at d = 128, 8 at d = 64) than the 256 CUs; then 128,
+    then 64.  The workspace follows the split length; grouped heads keep 1024."""
+    mha = B.make_layout(100, 16, 32, 128, 256)  # 4096 keys per sequence, 8 head groups
+    st = lambda batch, hq=32, layout=mha: lib.pa_decode_split_tokens(batch, hq,
+                                                                     ctypes.byref(layout))
+    assert st(2) == 256      # 2 x 16 splits x 8 groups = 256 units
+    assert st(1) == 128      # 1 x 16 x 8 = 128 < 256; 1 x 32 x 8 = 256
+    four = B.make_layout(100, 16, 4, 128, 1024)  # 16384 keys, 4 heads: one group
+    assert st(1, 4, four) == 64   # 64 and 128 units at 256 and 128 keys; 256 at 64
+    assert st(4, 4, four) == 256  # 4 x 64 x 1 = 256
+    d64 = B.make_layout(100, 16, 32, 64, 256)  # 8 heads per group: 4 groups
+    assert st(1, 32, d64) == 64   # 1 x 16 x 4 = 64, x 32 = 128, x 64 = 256
+    gl = B.make_layout(100, 16, 8, 128, 256)
+    assert st(1, 64, gl) == 1024
+    assert st(-1) == 0
+    # the workspace holds max_splits = 4096 / split partials per (sequence, head)
+    r = lambda n: (n + 255) // 256 * 256
+    need = r(1 * 32 * 32 * 128 * 4) + r(1 * 32 * 32 * 2 * 4) + r((2 + 32) * 4)
+    assert lib.pa_decode_workspace_bytes(1, 32, ctypes.byref(mha)) == need

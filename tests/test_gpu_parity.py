@@ -607,3 +607,32 @@ def test_decode_batch_at_the_api_limit(hq):
     seqs = sorted(set([0, 65534] + [int(x) for x in rng.integers(0, 65535, 398)]))
     G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, seqs=seqs),
               f"decode batch 65535 Hq={hq}")
+
+
+@pytest.mark.parametrize("batch,heads,d,lens,window,want", [
+    (2, 32, 128, [4096, 3000], 0, 256),     # 2 x 16 splits x 8 head groups = 256 units
+    (1, 32, 128, [4096], 0, 128),           # 128 units at 256 keys, 256 at 128
+    (1, 4, 128, [16384], 0, 64),            # one head group: 64 units at 256 keys
+    (1, 32, 64, [4096], 0, 64),             # d = 64: 4 groups of 8 heads
+    (1, 4, 128, [16384], 300, 64),          # windowed, laid back from the end
+    (3, 4, 128, [7000, 1, 16384], 1000, 128),  # 192 units at 256 keys, 384 at 128
+    (1, 32, 128, [4096], 5, 128),
+])
+def test_decode_split_lengths(batch, heads, d, lens, window, want):
+    """Small batches take 128- or 64-key decode splits so that pass 1 still has a unit
+    of work for every CU; each length (and the 256-key one) against the oracle."""
+    G.banner(f"decode split length batch={batch} heads={heads} d={d} lens={lens} "
+             f"window={window}")
+    wl = W.build("dsplit", 700 + len(lens) + heads + window, heads=heads, head_dim=d,
+                 page_size=16, lens=lens, kind="decode", pool_slack=1.2, device="cuda",
+                 poison=True)
+    call = wl.calls[0]
+    assert B.pa_decode_split_tokens(batch, heads, B.layout_of(wl.k_pool, call.block_table)) \
+        == want
+    out = torch.empty_like(call.q)
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale, out,
+                ws, window=window)
+    torch.cuda.synchronize()
+    G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, window=window),
+              f"decode split {want} window={window}")

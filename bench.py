@@ -422,7 +422,7 @@ def next_rows_summary(decode_wl, steps, warmup):
     nbytes = int(seen) * 2 * decode_wl.heads * decode_wl.head_dim * 2
     res["window_decode"] = _rate(nbytes, tm, HBM_PEAK_GBS, "GB/s", bound="hbm",
                                  workload=f"decode_64, window {w}",
-                                 kernel="decode_partial_kernel<128> + decode_combine_kernel<128>")
+                                 kernel=decode_kernel_name(decode_wl, call) + " + combine")
     del ws, out
 
     # f1: grouped heads

@@ -84,21 +84,34 @@ int check_scale(float scale) {
   return PA_OK;
 }
 
-// Units of pass-1 work below which the one-head-per-row decode shortens its splits: the
-// MI355X's 256 CUs each run one persistent workgroup that claims units.
+// Units of pass-1 work below which the decode shortens its splits: the MI355X has 256
+// CUs (the one-head-per-row decode runs one persistent workgroup per CU claiming units;
+// the grouped-head decode launches one workgroup per unit).
 constexpr int64_t kDecodeFillUnits = 256;
+// Query heads per workgroup of the grouped-head decode (kHeadBlock in decode_gqa.hip).
+constexpr int kGqaHeadBlock = 32;
 
 // Keys per decode split.  Grouped heads walk longer splits (their workgroups read a
 // quarter of the bytes per key that one-head-per-row workgroups do, so a longer split
-// keeps the per-workgroup set-up and merge small against the streaming).  The
-// one-head-per-row decode takes 256-key splits, halved (to 128, then 64) while a batch
-// of this many sequences, each as long as the table allows, would give pass 1 fewer
-// units (split x group of the heads one wave load covers) than there are CUs: a small
-// batch then still spreads over the chip instead of leaving CUs idle.
+// keeps the per-workgroup set-up and merge small against the streaming): 1024 keys,
+// halved (down to 128) while the batch, each sequence as long as the table allows,
+// would launch fewer workgroups (split x K/V head x block of 32 query heads) than there
+// are CUs.  The one-head-per-row decode takes 256-key splits, halved (to 128, then 64)
+// while the batch would give pass 1 fewer units (split x group of the heads one wave
+// load covers) than there are CUs.  Either way a small batch still spreads over the
+// chip instead of leaving CUs idle.
 int split_tokens_of(const pa_kv_layout* layout, int32_t num_q_heads, int32_t batch) {
-  if (num_q_heads / layout->num_kv_heads >= pa::kGqaMinGroup)
-    return pa::kDecodeSplitTokensGrouped;
   const int64_t tokens = (int64_t)layout->max_pages_per_seq * layout->page_size;
+  const int group = num_q_heads / layout->num_kv_heads;
+  if (group >= pa::kGqaMinGroup) {
+    const int64_t blocks =
+        (int64_t)layout->num_kv_heads * ((group + kGqaHeadBlock - 1) / kGqaHeadBlock);
+    int st = pa::kDecodeSplitTokensGrouped;
+    while (st > pa::kDecodeSplitTokensGrouped / 8 &&
+           (int64_t)batch * ((tokens + st - 1) / st) * blocks < kDecodeFillUnits)
+      st /= 2;
+    return st;
+  }
   const int heads_per_load = 64 / (layout->head_dim / 8);  // 4 at d = 128, 8 at d = 64
   const int64_t groups = (num_q_heads + heads_per_load - 1) / heads_per_load;
   int st = pa::kDecodeSplitTokens;

@@ -137,12 +137,15 @@ int pa_prefill(const pa_bf16* q, const pa_bf16* k_pool, const pa_bf16* v_pool,
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                  const pa_kv_layout* layout);
 
-/* Key positions covered by one decode split of a batch of `batch` sequences: 1024 when
- * num_q_heads / num_kv_heads >= 4; otherwise 256, halved to 128 and then 64 while
- * batch * ceil(max_pages_per_seq * page_size / split) * ceil(num_q_heads / h) < 256
- * (h = 4 heads at head_dim 128, 8 at 64: the heads one 1 KB wave load covers), so
- * that a small batch still gives each of the chip's 256 CUs a unit of work.  0 for an
- * invalid layout, head count or batch. */
+/* Key positions covered by one decode split of a batch of `batch` sequences, with
+ * T = max_pages_per_seq * page_size and g = num_q_heads / num_kv_heads:
+ *   g >= 4: 1024, halved down to 128 while
+ *           batch * ceil(T / split) * num_kv_heads * ceil(g / 32) < 256;
+ *   g < 4:  256, halved to 128 and then 64 while
+ *           batch * ceil(T / split) * ceil(num_q_heads / h) < 256
+ *           (h = 4 heads at head_dim 128, 8 at 64: the heads one 1 KB wave load covers),
+ * so that a small batch still gives each of the chip's 256 CUs work.  0 for an invalid
+ * layout, head count or batch. */
 int32_t pa_decode_split_tokens(int32_t batch, int32_t num_q_heads, const pa_kv_layout* layout);
 
 /*

@@ -269,8 +269,14 @@ def test_small_batches_take_shorter_decode_splits(lib):
     assert st(4, 4, four) == 256  # 4 x 64 x 1 = 256
     d64 = B.make_layout(100, 16, 32, 64, 256)  # 8 heads per group: 4 groups
     assert st(1, 32, d64) == 64   # 1 x 16 x 4 = 64, x 32 = 128, x 64 = 256
-    gl = B.make_layout(100, 16, 8, 128, 256)
-    assert st(1, 64, gl) == 1024
+    # grouped heads: 1024 keys, halved down to 128 while K/V heads x head blocks of 32 x
+    # splits x batch < 256 workgroups
+    gl = B.make_layout(100, 16, 8, 128, 256)   # 4096 keys, 8 K/V heads, g = 8: one block
+    assert st(1, 64, gl) == 128    # 32 and 64 and 128 workgroups at 1024, 512, 256 keys
+    assert st(8, 64, gl) == 1024   # 8 x 4 x 8 = 256
+    assert st(2, 64, gl) == 256    # 2 x 16 x 8 = 256
+    gl_long = B.make_layout(100, 16, 8, 128, 4096)  # 65536 keys
+    assert st(1, 64, gl_long) == 1024  # 64 splits x 8 = 512
     assert st(-1) == 0
     # the workspace holds max_splits = 4096 / split partials per (sequence, head)
     r = lambda n: (n + 255) // 256 * 256

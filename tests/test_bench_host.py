@@ -70,6 +70,12 @@ def test_gqa_threshold_matches_the_library():
     import re
     text = open(bench.os.path.join(bench.CSRC, "kernels.h")).read()
     assert int(re.search(r"kGqaMinGroup\s*=\s*(\d+)", text).group(1)) == bench.GQA_MIN_GROUP
+    # the host layer's split rule counts the grouped kernel's head blocks with the
+    # kernel's own block size
+    api = open(bench.os.path.join(bench.CSRC, "api.cpp")).read()
+    gqa = open(bench.os.path.join(bench.CSRC, "decode_gqa.hip")).read()
+    assert int(re.search(r"kGqaHeadBlock\s*=\s*(\d+)", api).group(1)) == \
+        int(re.search(r"kHeadBlock\s*=\s*(\d+)", gqa).group(1))
 
 
 def test_prefill_kernel_choice_matches_the_library():

@@ -617,17 +617,24 @@ def test_decode_batch_at_the_api_limit(hq):
     (1, 4, 128, [16384], 300, 64),          # windowed, laid back from the end
     (3, 4, 128, [7000, 1, 16384], 1000, 128),  # 192 units at 256 keys, 384 at 128
     (1, 32, 128, [4096], 5, 128),
+    # grouped heads (64 query heads over 8 K/V heads): 1024 keys, halved for small batches
+    (1, (8, 64), 128, [4096], 0, 128),
+    (2, (8, 64), 128, [4096, 2000], 0, 256),
+    (1, (8, 64), 128, [4096], 300, 128),
+    (8, (8, 64), 128, [4096] * 8, 0, 1024),
 ])
 def test_decode_split_lengths(batch, heads, d, lens, window, want):
-    """Small batches take 128- or 64-key decode splits so that pass 1 still has a unit
-    of work for every CU; each length (and the 256-key one) against the oracle."""
-    G.banner(f"decode split length batch={batch} heads={heads} d={d} lens={lens} "
+    """Small batches take shorter decode splits so that the chip's CUs all get work:
+    128 or 64 keys instead of 256, and down to 128 instead of 1024 with grouped heads;
+    each length against the oracle."""
+    hkv, hq = heads if isinstance(heads, tuple) else (heads, heads)
+    G.banner(f"decode split length batch={batch} Hkv={hkv} Hq={hq} d={d} lens={lens} "
              f"window={window}")
-    wl = W.build("dsplit", 700 + len(lens) + heads + window, heads=heads, head_dim=d,
+    wl = W.build("dsplit", 700 + len(lens) + hq + window, heads=hkv, head_dim=d,
                  page_size=16, lens=lens, kind="decode", pool_slack=1.2, device="cuda",
-                 poison=True)
+                 poison=True, q_heads=hq)
     call = wl.calls[0]
-    assert B.pa_decode_split_tokens(batch, heads, B.layout_of(wl.k_pool, call.block_table)) \
+    assert B.pa_decode_split_tokens(batch, hq, B.layout_of(wl.k_pool, call.block_table)) \
         == want
     out = torch.empty_like(call.q)
     ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)

@@ -100,6 +100,14 @@ constexpr int kGqaHeadBlock = 32;
 // while the batch would give pass 1 fewer units (split x group of the heads one wave
 // load covers) than there are CUs.  Either way a small batch still spreads over the
 // chip instead of leaving CUs idle.
+// Whether `batch` sequences of `tokens` keys in splits of `st` keys, times `width` work
+// items per split, make fewer than kDecodeFillUnits units (batch x splits < 2^40, and
+// width only multiplies a count already below the limit, so nothing overflows).
+bool too_few_units(int32_t batch, int64_t tokens, int st, int64_t width) {
+  const int64_t units = (int64_t)batch * ((tokens + st - 1) / st);
+  return units < kDecodeFillUnits && units * width < kDecodeFillUnits;
+}
+
 int split_tokens_of(const pa_kv_layout* layout, int32_t num_q_heads, int32_t batch) {
   const int64_t tokens = (int64_t)layout->max_pages_per_seq * layout->page_size;
   const int group = num_q_heads / layout->num_kv_heads;
@@ -107,17 +115,14 @@ int split_tokens_of(const pa_kv_layout* layout, int32_t num_q_heads, int32_t bat
     const int64_t blocks =
         (int64_t)layout->num_kv_heads * ((group + kGqaHeadBlock - 1) / kGqaHeadBlock);
     int st = pa::kDecodeSplitTokensGrouped;
-    while (st > pa::kDecodeSplitTokensGrouped / 8 &&
-           (int64_t)batch * ((tokens + st - 1) / st) * blocks < kDecodeFillUnits)
+    while (st > pa::kDecodeSplitTokensGrouped / 8 && too_few_units(batch, tokens, st, blocks))
       st /= 2;
     return st;
   }
   const int heads_per_load = 64 / (layout->head_dim / 8);  // 4 at d = 128, 8 at d = 64
   const int64_t groups = (num_q_heads + heads_per_load - 1) / heads_per_load;
   int st = pa::kDecodeSplitTokens;
-  while (st > pa::kDecodeSplitTokens / 4 &&
-         (int64_t)batch * ((tokens + st - 1) / st) * groups < kDecodeFillUnits)
-    st /= 2;
+  while (st > pa::kDecodeSplitTokens / 4 && too_few_units(batch, tokens, st, groups)) st /= 2;
   return st;
 }
 

@@ -14,9 +14,10 @@
 //     ceil(w / S) of them), times the head groups: a head group is the heads
 //     one wave load covers, 64 lanes x 16 B = 1 KB = one token's row for 4 adjacent
 //     heads at d = 128 (8 at d = 64), contiguous in the pool's [page, slot, head, d]
-//     layout.  A one-workgroup plan pass lists the pairs and zeroes a claim counter in
+//     layout.  A one-workgroup plan pass lists the pairs and sets a claim counter in
 //     the workspace.  Pass 1 then runs one persistent workgroup per CU: eight waves
-//     stream K/V, one more (the scheduler) claims units from the counter, resolves
+//     stream K/V, one more (the scheduler) claims units (its first two fixed by its
+//     index, the rest from the counter), resolves
 //     each (its sequence, its table pages "What is Paged FlashAttention?", "Practical
 //     example", its query slice) into an LDS descriptor a unit ahead, and merges and
 //     stores each finished unit's partial.  The streaming waves take 4 consecutive
@@ -122,13 +123,22 @@ __device__ __forceinline__ void split_range(int seq_len, int split, int window, 
   }
 }
 
+// The first claims of each pass-1 workgroup (the split it starts on and the one it
+// fetches ahead) are fixed: workgroup i takes units i and grid + i, and the counter
+// starts past them.  Through the counter, all workgroups would queue on one address at
+// launch.  Later claims stay on the counter: it keeps the workgroups running at one
+// moment on neighbouring units (the head groups of one split read the same token rows).
+constexpr int kFixedClaims = 2;
+
 // The list of (sequence, split) pairs holding keys, in sequence order, and the claim
-// counter of pass 1, both in the workspace: plan[0] = counter (zeroed here), plan[1] =
-// number of pairs, plan[2 + i] = pair i as the unsigned (sequence << 16) | split.  One workgroup
-// scans the sequences' split counts.
+// counter of pass 1, both in the workspace: plan[0] = counter (set here to
+// counter_start, the first unit no fixed claim takes), plan[1] = number of pairs,
+// plan[2 + i] = pair i as the unsigned (sequence << 16) | split.  One workgroup scans the
+// sequences' split counts.
 __global__ void __launch_bounds__(kPlanThreads)
 decode_plan_kernel(const int32_t* __restrict__ seq_lens, int batch, int split_tokens,
-                   int max_splits, int window, int32_t* __restrict__ plan) {
+                   int max_splits, int window, int counter_start,
+                   int32_t* __restrict__ plan) {
   __shared__ int scan[kPlanThreads];
   int base = 0;
   for (int c = 0; c < batch; c += kPlanThreads) {
@@ -168,13 +178,13 @@ decode_plan_kernel(const int32_t* __restrict__ seq_lens, int batch, int split_to
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    plan[0] = 0;
+    plan[0] = counter_start;
     plan[1] = base;
   }
 }
 
-// Pass 1: one persistent workgroup per CU.  The scheduler wave claims splits from the
-// plan's counter two ahead of the streaming waves, resolves each (sequence, table
+// Pass 1: one persistent workgroup per CU.  The scheduler wave claims splits (after the
+// fixed first two, from the plan's counter) two ahead of the streaming waves, resolves each (sequence, table
 // pages, query slice) into an LDS descriptor, and merges and writes the partial of the
 // split the streaming waves finished last; it issues every vector memory operation
 // besides the K/V stream, so the streaming waves' wait counts cover their own loads
@@ -204,10 +214,14 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     // ------------------------------------------------------------- scheduler wave
     const int n_items = plan[1] * n_hg;
     struct Claim { int valid, b, split, hg; };
+    int claims = 0;  // made so far; the first kFixedClaims take fixed units
     auto resolve = [&](SplitDesc& d) -> Claim {
-      int qi = 0;
-      if (lane == 0) qi = atomicAdd(&plan[0], 1);
-      qi = __builtin_amdgcn_readfirstlane(qi);
+      int qi = (int)blockIdx.x + claims * (int)gridDim.x;
+      if (claims >= kFixedClaims) {
+        if (lane == 0) qi = atomicAdd(&plan[0], 1);
+        qi = __builtin_amdgcn_readfirstlane(qi);
+      }
+      ++claims;
       Claim c{0, 0, 0, 0};
       if (qi >= n_items) {
         if (lane == 0) d.valid = 0;
@@ -561,9 +575,11 @@ int cu_count() {
 
 template <int D, int STEPS>
 void launch_partial(const DecodeArgs& a, hipStream_t stream) {
+  const int grid = cu_count();
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
-                     a.batch, a.split_tokens, a.max_splits, a.window, a.plan);
-  hipLaunchKernelGGL((decode_partial_kernel<D, STEPS>), dim3(cu_count()), dim3(kThreads), 0,
+                     a.batch, a.split_tokens, a.max_splits, a.window, kFixedClaims * grid,
+                     a.plan);
+  hipLaunchKernelGGL((decode_partial_kernel<D, STEPS>), dim3(grid), dim3(kThreads), 0,
                      stream,
                      a.q, a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
                      a.plan, score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,

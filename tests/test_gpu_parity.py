@@ -643,3 +643,39 @@ def test_decode_split_lengths(batch, heads, d, lens, window, want):
     torch.cuda.synchronize()
     G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call, window=window),
               f"decode split {want} window={window}")
+
+
+@pytest.mark.parametrize("offset", [(1, -1), (1, 0), (1, 1), (2, -1), (2, 0), (2, 1), (3, 5)])
+def test_decode_unit_counts_around_the_fixed_claims(offset):
+    """The persistent decode's workgroup i takes units i and grid + i without the claim
+    counter, which the plan starts at 2 x grid.  Unit counts just below, at and just
+    above one and two grids (some workgroups find one or both fixed units empty; the
+    counter hands out nothing, one unit or more) each against the oracle: 4 heads at
+    d = 128 are one head group, so the units are the (sequence, 256-key split) pairs."""
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    mult, extra = offset
+    target = mult * grid + extra
+    batch = 64
+    assert batch <= target <= 16 * batch
+    rng = np.random.default_rng(target)
+    splits = [16] + [1] * (batch - 1)  # one 4096-key sequence keeps the split at 256
+    left = target - sum(splits)
+    while left > 0:
+        b = int(rng.integers(1, batch))
+        if splits[b] < 16:
+            splits[b] += 1
+            left -= 1
+    lens = [256 * (n - 1) + int(rng.integers(1, 257)) for n in splits]
+    G.banner(f"decode unit count {target} (grid {grid}): lens={lens[:8]}...")
+    wl = W.build("dclaims", 800 + target, heads=4, head_dim=128, page_size=16, lens=lens,
+                 kind="decode", pool_slack=1.2, device="cuda", poison=True)
+    call = wl.calls[0]
+    assert B.pa_decode_split_tokens(batch, 4, B.layout_of(wl.k_pool, call.block_table)) == 256
+    out = torch.empty_like(call.q)
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    for rnd in range(2):  # the second call finds the counter where the first left it
+        out.fill_(float("nan"))
+        B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale,
+                    out, ws)
+        torch.cuda.synchronize()
+        G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), f"units={target} call {rnd}")

@@ -15,7 +15,8 @@
 //     one wave load covers, 64 lanes x 16 B = 1 KB = one token's row for 4 adjacent
 //     heads at d = 128 (8 at d = 64), contiguous in the pool's [page, slot, head, d]
 //     layout.  A one-workgroup plan pass lists the pairs and sets a claim counter in
-//     the workspace.  Pass 1 then runs one persistent workgroup per CU: eight waves
+//     the workspace (skipped when every split slot of every sequence fits the fixed
+//     claims below: the workgroups then enumerate their units in place).  Pass 1 then runs one persistent workgroup per CU: eight waves
 //     stream K/V, one more (the scheduler) claims units (its first two fixed by its
 //     index, the rest from the counter), resolves
 //     each (its sequence, its table pages "What is Paged FlashAttention?", "Practical
@@ -123,6 +124,14 @@ __device__ __forceinline__ void split_range(int seq_len, int split, int window, 
   }
 }
 
+// Splits of a sequence of len keys that hold keys (inside the window, if any), at most
+// max_splits: the plan and the partials hold max_splits per sequence.
+__device__ inline int sequence_splits(int len, int window, int split_tokens, int max_splits) {
+  const int n = window > 0 ? window_split_count(len, window, split_tokens)
+                           : (len > 0 ? (len + split_tokens - 1) / split_tokens : 0);
+  return min(n, max_splits);
+}
+
 // The first claims of each pass-1 workgroup (the split it starts on and the one it
 // fetches ahead) are fixed: workgroup i takes units i and grid + i, and the counter
 // starts past them.  Through the counter, all workgroups would queue on one address at
@@ -144,12 +153,7 @@ decode_plan_kernel(const int32_t* __restrict__ seq_lens, int batch, int split_to
   for (int c = 0; c < batch; c += kPlanThreads) {
     const int b = c + (int)threadIdx.x;
     int n = 0;
-    if (b < batch) {
-      const int len = seq_lens[b];
-      n = window > 0 ? window_split_count(len, window, split_tokens)
-                     : (len > 0 ? (len + split_tokens - 1) / split_tokens : 0);
-      n = min(n, max_splits);  // the plan and the partials hold max_splits per sequence
-    }
+    if (b < batch) n = sequence_splits(seq_lens[b], window, split_tokens, max_splits);
     scan[threadIdx.x] = n;
     __syncthreads();
     for (int off = 1; off < kPlanThreads; off <<= 1) {
@@ -197,7 +201,7 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       const int32_t* __restrict__ seq_lens, float* __restrict__ ws_o,
                       float* __restrict__ ws_ml, int32_t* __restrict__ plan,
                       float scale_log2, int num_q_heads, int num_kv_heads, int log2_ps,
-                      int max_pages, int max_splits, int window) {
+                      int max_pages, int max_splits, int window, int in_place_batch) {
   using G = DecodeGeometry<D>;
   using SS = SplitShape<STEPS>;
   constexpr uint32_t kOutside = 0x80000000u;   // a load offset past every buffer
@@ -212,23 +216,40 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   if (wave == kStreamWaves) {
     // ------------------------------------------------------------- scheduler wave
-    const int n_items = plan[1] * n_hg;
+    // in place: the units are every (sequence, split slot, head group), at most
+    // kFixedClaims per workgroup, and no plan was written
+    const int n_items =
+        in_place_batch > 0 ? in_place_batch * max_splits * n_hg : plan[1] * n_hg;
     struct Claim { int valid, b, split, hg; };
     int claims = 0;  // made so far; the first kFixedClaims take fixed units
     auto resolve = [&](SplitDesc& d) -> Claim {
-      int qi = (int)blockIdx.x + claims * (int)gridDim.x;
-      if (claims >= kFixedClaims) {
-        if (lane == 0) qi = atomicAdd(&plan[0], 1);
-        qi = __builtin_amdgcn_readfirstlane(qi);
-      }
-      ++claims;
       Claim c{0, 0, 0, 0};
-      if (qi >= n_items) {
+      if (in_place_batch > 0) {
+        // this workgroup's fixed units in turn, skipping split slots with no keys
+        while (!c.valid && claims < kFixedClaims) {
+          const int qi = (int)blockIdx.x + claims * (int)gridDim.x;
+          ++claims;
+          if (qi >= n_items) break;
+          const int p = qi / n_hg;
+          c = Claim{0, p / max_splits, p % max_splits, qi % n_hg};
+          c.valid = c.split < sequence_splits(seq_lens[c.b], window, SS::kTokens, max_splits);
+        }
+      } else {
+        int qi = (int)blockIdx.x + claims * (int)gridDim.x;
+        if (claims >= kFixedClaims) {
+          if (lane == 0) qi = atomicAdd(&plan[0], 1);
+          qi = __builtin_amdgcn_readfirstlane(qi);
+        }
+        ++claims;
+        if (qi < n_items) {
+          const uint32_t pair = (uint32_t)plan[2 + qi / n_hg];
+          c = Claim{1, (int)(pair >> 16), (int)(pair & 0xffffu), qi % n_hg};
+        }
+      }
+      if (!c.valid) {
         if (lane == 0) d.valid = 0;
         return c;
       }
-      const uint32_t pair = (uint32_t)plan[2 + qi / n_hg];
-      c = Claim{1, (int)(pair >> 16), (int)(pair & 0xffffu), qi % n_hg};
       const int seq_len = seq_lens[c.b];
       int t_begin, t_end;
       split_range<SS::kTokens>(seq_len, c.split, window, t_begin, t_end);
@@ -575,15 +596,23 @@ int cu_count() {
 
 template <int D, int STEPS>
 void launch_partial(const DecodeArgs& a, hipStream_t stream) {
+  using G = DecodeGeometry<D>;
   const int grid = cu_count();
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
-                     a.batch, a.split_tokens, a.max_splits, a.window, kFixedClaims * grid,
-                     a.plan);
+  // when every (sequence, split slot, head group) fits the fixed claims, the workgroups
+  // enumerate their units in place and the plan pass is not needed
+  const int64_t slots = (int64_t)a.batch * a.max_splits *
+                        ((a.num_q_heads + G::kHeads - 1) / G::kHeads);
+  const int in_place_batch = slots <= (int64_t)kFixedClaims * grid ? a.batch : 0;
+  if (in_place_batch == 0)
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
+                       a.batch, a.split_tokens, a.max_splits, a.window, kFixedClaims * grid,
+                       a.plan);
   hipLaunchKernelGGL((decode_partial_kernel<D, STEPS>), dim3(grid), dim3(kThreads), 0,
                      stream,
                      a.q, a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.ws_o, a.ws_ml,
                      a.plan, score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
-                     a.log2_page_size, a.max_pages_per_seq, a.max_splits, a.window);
+                     a.log2_page_size, a.max_pages_per_seq, a.max_splits, a.window,
+                     in_place_batch);
 }
 
 }  // namespace

@@ -679,3 +679,35 @@ def test_decode_unit_counts_around_the_fixed_claims(offset):
                     out, ws)
         torch.cuda.synchronize()
         G.compare(G.bf16_out_to_f64(out), G.oracle_for(wl, call), f"units={target} call {rnd}")
+
+
+@pytest.mark.parametrize("lens,window", [([4096, 0, 1, 700], 0), ([4096, 0, 1, 700], 300),
+                                         ([1, 2, 3000], 0), ([9000, 65], 1000)])
+def test_small_batch_decode_without_plan(lens, window):
+    """A batch whose (sequence, split slot, head group) space fits two units per CU runs
+    pass 1 without the plan: each workgroup takes its two units by index and skips split
+    slots with no keys (an empty sequence, a one-key one, slots before a window), so a
+    workgroup may find its first unit empty and its second full.  Against the oracle,
+    twice in a row on one workspace."""
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    G.banner(f"small-batch decode without the plan: lens={lens} window={window}")
+    wl = W.build("noplan", 850 + len(lens) + window, heads=4, head_dim=128, page_size=16,
+                 lens=lens, kind="decode", pool_slack=1.2, device="cuda", poison=True)
+    call = wl.calls[0]
+    lay = B.layout_of(wl.k_pool, call.block_table)
+    split = B.pa_decode_split_tokens(len(lens), 4, lay)
+    slots = len(lens) * -(-call.block_table.shape[1] * 16 // split)  # one head group
+    assert slots <= 2 * grid, "this case is meant for the plan-free path"
+    out = torch.empty_like(call.q)
+    ws = B.decode_workspace(call.q, wl.k_pool, call.block_table)
+    for rnd in range(2):
+        out.fill_(float("nan"))
+        B.pa_decode(call.q, wl.k_pool, wl.v_pool, call.block_table, call.seq_lens, wl.scale,
+                    out, ws, window=window)
+        torch.cuda.synchronize()
+        got = G.bf16_out_to_f64(out)
+        live = [b for b, L in enumerate(lens) if L > 0]
+        empty = [b for b, L in enumerate(lens) if L == 0]
+        assert np.all(got[empty] == 0.0)
+        G.compare(got, G.oracle_for(wl, call, seqs=live, window=window),
+                  f"no plan lens={lens} window={window} call {rnd}")

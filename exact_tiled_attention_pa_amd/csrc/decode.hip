@@ -15,8 +15,8 @@
 //     one wave load covers, 64 lanes x 16 B = 1 KB = one token's row for 4 adjacent
 //     heads at d = 128 (8 at d = 64), contiguous in the pool's [page, slot, head, d]
 //     layout.  A one-workgroup plan pass lists the pairs and sets a claim counter in
-//     the workspace (skipped when every split slot of every sequence fits the fixed
-//     claims below: the workgroups then enumerate their units in place).  Pass 1 then runs one persistent workgroup per CU: eight waves
+//     the workspace (skipped when the split slots of all sequences, times the head
+//     groups, are at most one per workgroup: workgroup i then takes unit i in place).  Pass 1 then runs one persistent workgroup per CU: eight waves
 //     stream K/V, one more (the scheduler) claims units (its first two fixed by its
 //     index, the rest from the counter), resolves
 //     each (its sequence, its table pages "What is Paged FlashAttention?", "Practical
@@ -216,8 +216,8 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   if (wave == kStreamWaves) {
     // ------------------------------------------------------------- scheduler wave
-    // in place: the units are every (sequence, split slot, head group), at most
-    // kFixedClaims per workgroup, and no plan was written
+    // in place: the units are every (sequence, split slot, head group), at most one
+    // per workgroup, and no plan was written
     const int n_items =
         in_place_batch > 0 ? in_place_batch * max_splits * n_hg : plan[1] * n_hg;
     struct Claim { int valid, b, split, hg; };
@@ -225,11 +225,10 @@ decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     auto resolve = [&](SplitDesc& d) -> Claim {
       Claim c{0, 0, 0, 0};
       if (in_place_batch > 0) {
-        // this workgroup's fixed units in turn, skipping split slots with no keys
-        while (!c.valid && claims < kFixedClaims) {
-          const int qi = (int)blockIdx.x + claims * (int)gridDim.x;
-          ++claims;
-          if (qi >= n_items) break;
+        // unit i is workgroup i's only one; a split slot holding no keys of its
+        // sequence leaves the workgroup without work
+        const int qi = claims++ == 0 ? (int)blockIdx.x : n_items;
+        if (qi < n_items) {
           const int p = qi / n_hg;
           c = Claim{0, p / max_splits, p % max_splits, qi % n_hg};
           c.valid = c.split < sequence_splits(seq_lens[c.b], window, SS::kTokens, max_splits);
@@ -598,11 +597,14 @@ template <int D, int STEPS>
 void launch_partial(const DecodeArgs& a, hipStream_t stream) {
   using G = DecodeGeometry<D>;
   const int grid = cu_count();
-  // when every (sequence, split slot, head group) fits the fixed claims, the workgroups
-  // enumerate their units in place and the plan pass is not needed
+  // when the (sequence, split slot, head group) space holds at most one unit per
+  // workgroup, workgroup i takes unit i in place and the plan pass is not needed.  Not
+  // with two per workgroup: the slots holding keys are a prefix of each sequence's
+  // range, so by index some workgroups could get two units where the plan gives none
+  // more than one
   const int64_t slots = (int64_t)a.batch * a.max_splits *
                         ((a.num_q_heads + G::kHeads - 1) / G::kHeads);
-  const int in_place_batch = slots <= (int64_t)kFixedClaims * grid ? a.batch : 0;
+  const int in_place_batch = slots <= grid ? a.batch : 0;
   if (in_place_batch == 0)
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.seq_lens,
                        a.batch, a.split_tokens, a.max_splits, a.window, kFixedClaims * grid,

@@ -6,9 +6,8 @@
 
 namespace pa {
 
-// 32 query rows per workgroup, shared by 4 waves that divide the key tiles among
-// themselves and merge their softmax states at the end.
-constexpr int kPrefillSplitWaves = 4;
+// 32 query rows per workgroup, shared by its waves (8 at head_dim 64, 5 at 128), which
+// divide the key tiles among themselves and merge their softmax states at the end.
 constexpr int kPrefillSplitBlockM = 32;
 // Its LDS holds one workgroup per CU: the automatic choice takes it when its grid fits
 // the 256 CUs at once and a sequence may span more than one key tile.

@@ -9,16 +9,16 @@
 // their key tiles one after another, so a launch's duration is at least its longest key
 // loop: for the 600-token example of one head that is 5 workgroups on a chip of 256
 // CUs, the last of them walking 10 tiles alone.  Here a workgroup holds only 32 query
-// rows and its four waves share them: wave w walks key tiles w, w + 4, w + 8, ... of the
-// rows' visible range, each with its own online-softmax state (running max, running
+// rows and its W waves share them (W = 8 at head_dim 64, 5 at 128: as many as the CU's
+// LDS holds): wave w walks key tiles w, w + W, w + 2W, ... of the rows' visible range, each with its own online-softmax state (running max, running
 // sum, unnormalised output; "Flash Attention: Fast, Memory-Efficient Attention for
-// LLMs", "The Algorithm"), and at the end the four states are merged with the same
+// LLMs", "The Algorithm"), and at the end the W states are merged with the same
 // rescaling algebra a split decode uses (states relative to maxima m_w combine as
-// sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w with M = max_w m_w).  The key loop is a
-// quarter as long, and the launch has four times as many workgroups.
+// sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w with M = max_w m_w).  The key loop is
+// 1/W as long, and the launch has four times as many workgroups.
 //
-// Per wave: its own LDS stages (two at head_dim 64, one at 128: 128 KB per workgroup,
-// one workgroup per CU), filled by buffer loads straight into LDS with rows past the
+// Per wave: one LDS stage of a K and a V tile (16 KB at head_dim 64, 32 KB at 128: 128
+// and 160 KB per workgroup, one workgroup per CU), filled by buffer loads straight into LDS with rows past the
 // sequence end reading as zero, waited for with the wave's own load counter (no
 // workgroup barrier until the merge).  The tile arithmetic is prefill_kernel's: S^T = K
 // Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, the transposing LDS read for V^T,
@@ -35,8 +35,6 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = kPrefillSplitWaves;   // waves sharing a workgroup's query rows
-constexpr int kThreads = 64 * kWaves;
 constexpr int BM = kPrefillSplitBlockM;      // 32 query rows per workgroup
 constexpr int BN = kPrefillBlockN;           // 64 key positions per tile
 constexpr int kRescaleThreshold = 8;
@@ -49,7 +47,13 @@ struct SplitGeometry {
   static constexpr int kInstPerTile = BN / kRowsPerInst;  // loads per K (or V) tile
   static constexpr int kInstPerGroup = 16 / kRowsPerInst; // loads per 16-row group
   static constexpr int kTileBytes = BN * kRowBytes;
-  static constexpr int kStages = D == 64 ? 2 : 1;         // LDS stages per wave
+  // waves sharing the rows: one stage of 2 * kTileBytes each, as many as the CU's 160 KB
+  // of LDS holds (8 x 16 KB at d = 64; 5 x 32 KB at d = 128).  Against 4 waves with two
+  // stages at d = 64: the 600-token example 6.5 -> 5.9 us, 33 rows over 9,000 keys 44 ->
+  // 23 us; 300 rows over 3,000 keys at d = 128 24.2 -> 20.4 us
+  static constexpr int kWaves = D == 64 ? 8 : 5;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kStages = 1;                       // LDS stages per wave
   static constexpr int kWaveBytes = kStages * 2 * kTileBytes;
   static constexpr int kDK = D / 16;                      // MFMA k-steps over d
   static constexpr int kDB = D / 32;                      // 32-wide output blocks
@@ -57,16 +61,16 @@ struct SplitGeometry {
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(SplitGeometry<D>::kThreads)
 prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
                      const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
                      const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_start,
                      uint16_t* __restrict__ out, float scale_log2, int num_q_heads,
                      int num_kv_heads, int log2_ps, int max_pages, int window) {
   using G = SplitGeometry<D>;
-  static_assert(kWaves * G::kWaveBytes <= 160 * 1024, "LDS of one CU");
-  static_assert(kWaves * BM * G::kMergeRow * 4 <= kWaves * G::kWaveBytes, "merge fits");
-  __shared__ __attribute__((aligned(1024))) char lds[kWaves * G::kWaveBytes];
+  static_assert(G::kWaves * G::kWaveBytes <= 160 * 1024, "LDS of one CU");
+  static_assert(G::kWaves * BM * G::kMergeRow * 4 <= G::kWaves * G::kWaveBytes, "merge fits");
+  __shared__ __attribute__((aligned(1024))) char lds[G::kWaves * G::kWaveBytes];
 
   const int h = blockIdx.x;
   const int b = blockIdx.z;
@@ -314,18 +318,18 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[c][db], pb[c], oacc[db], 0, 0, 0);
   };
 
-  // ---- this wave's key tiles: first_tile + wave, + kWaves, ... below n_tiles
+  // ---- this wave's key tiles: first_tile + wave, + G::kWaves, ... below n_tiles
   const int j0 = first_tile + wave;
-  const int count = j0 < n_tiles ? (n_tiles - j0 + kWaves - 1) / kWaves : 0;
+  const int count = j0 < n_tiles ? (n_tiles - j0 + G::kWaves - 1) / G::kWaves : 0;
   constexpr int kLoadsPerTile = 2 * G::kInstPerTile;
   static_assert(kLoadsPerTile <= 63, "a tile's loads fit the load counter");
   if (count > 0) {
     fetch_table(j0);
     issue_tile(j0, 0);
-    if (count > 1) fetch_table(j0 + kWaves);
+    if (count > 1) fetch_table(j0 + G::kWaves);
   }
   for (int it = 0; it < count; ++it) {
-    const int j = j0 + it * kWaves;
+    const int j = j0 + it * G::kWaves;
     const int s = it % G::kStages;
     const bool more = it + 1 < count;
     if constexpr (G::kStages == 2) {
@@ -335,8 +339,8 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       if (more) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __asm__ __volatile__("" ::: "memory");
-        issue_tile(j + kWaves, 1 - s);
-        if (it + 2 < count) fetch_table(j + 2 * kWaves);
+        issue_tile(j + G::kWaves, 1 - s);
+        if (it + 2 < count) fetch_table(j + 2 * G::kWaves);
       }
       if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -350,8 +354,8 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // tile's loads overwrite it
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __asm__ __volatile__("" ::: "memory");
-        issue_tile(j + kWaves, 0);
-        if (it + 2 < count) fetch_table(j + 2 * kWaves);
+        issue_tile(j + G::kWaves, 0);
+        if (it + 2 < count) fetch_table(j + 2 * G::kWaves);
       }
     }
     finish_tile(j);
@@ -381,22 +385,22 @@ prefill_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   __syncthreads();
   constexpr int kPieces = BM * G::kChunks;  // 16-byte output pieces of the 32 rows
 #pragma unroll
-  for (int p = tid; p < kPieces; p += kThreads) {
+  for (int p = tid; p < kPieces; p += G::kThreads) {
     const int r = p / G::kChunks;
     const int c = p % G::kChunks;
     const int qrow = q0 + r;
     if (qrow >= q_len) continue;
-    float mw[kWaves];
+    float mw[G::kWaves];
     float mmax = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < G::kWaves; ++w) {
       mw[w] = st[(w * BM + r) * G::kMergeRow + D];
       mmax = fmaxf(mmax, mw[w]);
     }
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float l = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < G::kWaves; ++w) {
       // a wave that saw no visible key of this row holds O = 0, l = 0 and m = -inf
       const float a = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - mmax);
       const float* src = st + (w * BM + r) * G::kMergeRow;
@@ -420,7 +424,7 @@ template <int D, bool CAUSAL>
 void launch(const PrefillArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.max_q_len + BM - 1) / BM;
   const dim3 grid(a.num_q_heads, n_qtiles, a.batch);
-  hipLaunchKernelGGL((prefill_split_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a.q,
+  hipLaunchKernelGGL((prefill_split_kernel<D, CAUSAL>), grid, dim3(SplitGeometry<D>::kThreads), 0, stream, a.q,
                      a.k_pool, a.v_pool, a.block_table, a.seq_lens, a.q_start, a.out,
                      score_scale_log2(a.scale), a.num_q_heads, a.num_kv_heads,
                      a.log2_page_size, a.max_pages_per_seq, a.window);

@@ -111,8 +111,8 @@ typedef struct pa_kv_layout {
  * q, k_pool, v_pool and out must be 16-byte aligned (the kernels move 16-byte pieces).
  * Two kernels compute the same attention: a tiled one (128 query rows per workgroup,
  * their key tiles walked in order) and a split-key one for launches too small to fill
- * the chip (32 query rows per workgroup whose four waves divide the key tiles and
- * merge their softmax states).  The split-key kernel runs when
+ * the chip (32 query rows per workgroup whose waves, 8 at head_dim 64 and 5 at 128,
+ * divide the key tiles and merge their softmax states).  The split-key kernel runs when
  * num_q_heads * batch * ceil(max_q_len / 32) <= 256 and max_pages_per_seq * page_size
  * > 64; the environment variable PA_PREFILL_PATH, read at each call, forces one
  * ("tiles" or "split"; unset, empty or "auto": the rule above).  The two round

@@ -1,5 +1,5 @@
 """The split-key prefill kernel (32 query rows per workgroup, the key tiles dealt over
-its four waves, the waves' softmax states merged at the end) against the fp64 oracle,
+its waves, eight at d = 64 and five at d = 128, the waves' softmax states merged at the end) against the fp64 oracle,
 the automatic choice between it and the 128-row tiled kernel, and the binding's
 prepared calls (PreparedPrefill, PreparedDecode) against the direct ones.
 

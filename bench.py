@@ -174,7 +174,7 @@ def decode_kind(wl) -> str:
 # kernel when its grid of 32-row workgroups fits one per CU and a sequence may span more
 # than one 64-key tile, unless PA_PREFILL_PATH forces one
 PREFILL_SPLIT_BLOCK_M = 32
-PREFILL_SPLIT_MAX_WORKGROUPS = 256
+PREFILL_SPLIT_MAX_WORKGROUPS = 512
 
 
 def prefill_takes_split(wl, call) -> bool:

@@ -10,8 +10,12 @@ namespace pa {
 // divide the key tiles among themselves and merge their softmax states at the end.
 constexpr int kPrefillSplitBlockM = 32;
 // Its LDS holds one workgroup per CU: the automatic choice takes it when its grid fits
-// the 256 CUs at once and a sequence may span more than one key tile.
-constexpr int kPrefillSplitMaxWorkgroups = 256;
+// two rounds of the 256 CUs and a sequence may span more than one key tile.  Measured
+// with both kernels forced (causal, d = 128, one sequence): 16 heads x 1024 rows (512
+// split workgroups) 22.7 us tiled, 16.1 split; 8 x 2048 (512) 40.3, 21.1; 32 x 1024
+// (1024) 23.5, 28.8; 64-row chunks of 8 sequences on 4096-key caches, 32 heads (512)
+// 116.6, 120.6.
+constexpr int kPrefillSplitMaxWorkgroups = 512;
 
 // Which prefill kernel runs: chosen by launch size, or forced to one of the two.
 constexpr int kPrefillPathAuto = 0;

@@ -113,7 +113,7 @@ typedef struct pa_kv_layout {
  * their key tiles walked in order) and a split-key one for launches too small to fill
  * the chip (32 query rows per workgroup whose waves, 8 at head_dim 64 and 5 at 128,
  * divide the key tiles and merge their softmax states).  The split-key kernel runs when
- * num_q_heads * batch * ceil(max_q_len / 32) <= 256 and max_pages_per_seq * page_size
+ * num_q_heads * batch * ceil(max_q_len / 32) <= 512 and max_pages_per_seq * page_size
  * > 64; the environment variable PA_PREFILL_PATH, read at each call, forces one
  * ("tiles" or "split"; unset, empty or "auto": the rule above).  The two round
  * differently, each within the same tolerance of the exact result.

@@ -71,11 +71,11 @@ def test_split_kernel_window_one_returns_own_value_row(monkeypatch):
         assert torch.equal(out[i], wl.v_pool[int(bt[t // 16]), t % 16]), i
 
 
-@pytest.mark.parametrize("which", ["prefill_600", "tiny_heads", "large"])
+@pytest.mark.parametrize("which", ["prefill_600", "tiny_heads", "mid", "large"])
 def test_automatic_choice_follows_the_launch_size(which, monkeypatch):
-    """With PA_PREFILL_PATH unset, a launch whose 32-row grid fits one workgroup per CU
-    (the worked example: 19 workgroups; 4 heads x 600 rows: 76) runs the split-key kernel
-    and a larger one (32 heads x 1024 rows: 1024 workgroups) the tiled kernel.  The two
+    """With PA_PREFILL_PATH unset, a launch whose 32-row grid is at most 512 workgroups
+    (the worked example: 19; 4 heads x 600 rows: 76; 16 heads x 1024 rows: 512) runs the
+    split-key kernel and a larger one (32 heads x 1024 rows: 1024) the tiled kernel.  The two
     kernels round differently, so the automatic output equals exactly one forced path's
     output bit for bit (and matches the oracle)."""
     G.banner(f"automatic prefill kernel choice: {which}")
@@ -85,6 +85,10 @@ def test_automatic_choice_follows_the_launch_size(which, monkeypatch):
     elif which == "tiny_heads":
         wl = W.build("auto4", 55, heads=4, head_dim=128, page_size=256, lens=[600],
                      q_lens=[600], causal=True, device="cuda", poison=True)
+        want = "split"
+    elif which == "mid":
+        wl = W.build("auto16", 57, heads=16, head_dim=128, page_size=256, lens=[1024],
+                     q_lens=[1024], causal=True, device="cuda", poison=True)
         want = "split"
     else:
         wl = W.build("auto32", 56, heads=32, head_dim=128, page_size=256, lens=[1024],
@@ -98,7 +102,7 @@ def test_automatic_choice_follows_the_launch_size(which, monkeypatch):
     other = "tiles" if want == "split" else "split"
     assert torch.equal(outs["auto"], outs[want])
     assert not torch.equal(outs[want], outs[other]), "the two kernels agreed bit for bit"
-    if which != "large":
+    if which not in ("large", "mid"):
         G.compare(G.bf16_out_to_f64(outs["auto"]), G.oracle_for(wl, call), which)
     else:
         rows = {0: G.spread_rows(1024, 256, seed=3)}
